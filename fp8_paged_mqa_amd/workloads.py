@@ -1,0 +1,225 @@
+"""Seeded synthetic inputs for the paged MQA indexer (logits + top-k).
+
+This module only draws and lays out inputs: it holds none of the method's
+arithmetic (no decode, no dot product, no selection). Values are drawn in
+float32 and encoded to e4m3fn bytes with torch's CPU cast (round to nearest
+even); everything downstream sees bytes. Tests, the benchmark and the smoke
+check all build their inputs here, so the HIP path and the CPU oracle always
+see identical bytes.
+
+Layouts (the calling convention of the paged indexer in the stepcodex.com
+issue "[Bug] aiter ops triton attention pa_mqa_logits", section "Minimal
+reproduction"):
+  q             uint8 [B, N, H, 128]   e4m3fn
+  kv_cache      uint8 [num_blocks, 132] 128 e4m3fn key bytes + fp32 scale (LE)
+  weights       f32   [B*N, H]
+  context_lens  i32   [B]
+  block_tables  i32   [B, W]           slots t >= ctx hold -1
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+HEAD_DIM = 128
+ROW_BYTES = HEAD_DIM + 4
+TOPK = 2048
+
+
+@dataclass
+class Workload:
+    name: str
+    q: np.ndarray
+    kv_cache: np.ndarray
+    weights: np.ndarray
+    context_lens: np.ndarray
+    block_tables: np.ndarray
+    max_model_len: int
+    next_n: int
+    k: int = TOPK
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def heads(self) -> int:
+        return int(self.q.shape[2])
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.next_n
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.kv_cache.shape[0])
+
+    @property
+    def sum_ctx(self) -> int:
+        return int(self.context_lens.astype(np.int64).sum())
+
+    def visible(self) -> np.ndarray:
+        """Visible positions per row: max(0, min(ctx - N + j + 1, L))."""
+        ctx = np.repeat(self.context_lens.astype(np.int64), self.next_n)
+        j = np.tile(np.arange(self.next_n), self.batch)
+        return np.clip(ctx - self.next_n + j + 1, 0, self.max_model_len)
+
+
+def to_e4m3fn_bytes(x: np.ndarray) -> np.ndarray:
+    """float32 -> e4m3fn bytes via torch's CPU cast (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def _kv_rows(key_bytes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    rows = np.empty((key_bytes.shape[0], ROW_BYTES), dtype=np.uint8)
+    rows[:, :HEAD_DIM] = key_bytes
+    rows[:, HEAD_DIM:] = np.ascontiguousarray(scales, dtype="<f4").view(np.uint8).reshape(-1, 4)
+    return rows
+
+
+def _poison_rows(kv: np.ndarray, used: np.ndarray) -> None:
+    """Unreferenced rows become NaN keys (0x7F) with a NaN scale, so that a
+    gather from a wrong row cannot go unnoticed."""
+    unused = np.ones(kv.shape[0], dtype=bool)
+    unused[used] = False
+    kv[unused, :HEAD_DIM] = 0x7F
+    kv[unused, HEAD_DIM:] = np.frombuffer(np.float32(np.nan).tobytes(), dtype=np.uint8)
+
+
+def _tables_from_assignment(ctx: np.ndarray, width: int, assign) -> np.ndarray:
+    bt = np.full((ctx.size, width), -1, dtype=np.int32)
+    for b, c in enumerate(ctx.tolist()):
+        bt[b, :c] = assign(b, c)
+    return bt
+
+
+def build(name, rng, *, batch, next_n, heads, ctx, max_model_len, pool, table,
+          table_width=None, outlier_frac=0.0, poison_unused=True, k=TOPK,
+          key_fn=None, scale_fn=None, q_fn=None, w_fn=None) -> Workload:
+    """Draws a workload in the fixed order ctx -> tables -> q -> K -> scales ->
+    outliers -> weights. ``ctx`` is an int array already drawn by the caller.
+
+    table: "identity"  request b reads rows [0, ctx_b) (every request the same)
+           "permuted"  one permutation of the pool, sliced per request in order
+           "interleaved" one permutation, dealt out token by token across the
+                       requests still running (for t, for b with ctx_b > t)
+    """
+    ctx = np.asarray(ctx, dtype=np.int32)
+    width = int(table_width or max(1, int(ctx.max(initial=1))))
+    if table == "identity":
+        bt = _tables_from_assignment(ctx, width, lambda b, c: np.arange(c))
+    elif table == "permuted":
+        perm = rng.permutation(pool).astype(np.int32)
+        offs = np.concatenate([[0], np.cumsum(ctx.astype(np.int64))])
+        assert offs[-1] <= pool, "pool smaller than the sum of context lengths"
+        bt = _tables_from_assignment(ctx, width, lambda b, c: perm[offs[b]:offs[b] + c])
+    elif table == "interleaved":
+        perm = rng.permutation(pool).astype(np.int32)
+        b_idx = np.repeat(np.arange(ctx.size), ctx)
+        t_idx = np.concatenate([np.arange(c) for c in ctx.tolist()]) if ctx.size else np.zeros(0, int)
+        order = np.lexsort((b_idx, t_idx))            # token-major, then request
+        assert order.size <= pool
+        bt = np.full((ctx.size, width), -1, dtype=np.int32)
+        bt[b_idx[order], t_idx[order]] = perm[:order.size]
+    else:
+        raise ValueError(table)
+
+    rows = batch * next_n
+    q_f = q_fn(rng, (batch, next_n, heads, HEAD_DIM)) if q_fn else \
+        rng.standard_normal((batch, next_n, heads, HEAD_DIM), dtype=np.float32)
+    k_f = key_fn(rng, (pool, HEAD_DIM)) if key_fn else \
+        rng.standard_normal((pool, HEAD_DIM), dtype=np.float32)
+    scales = scale_fn(rng, pool) if scale_fn else \
+        rng.lognormal(0.0, 0.5, size=pool).astype(np.float32)
+    if outlier_frac > 0:
+        hot = rng.random(pool) < outlier_frac
+        k_f[hot] *= 8.0
+    weights = w_fn(rng, (rows, heads)) if w_fn else \
+        rng.standard_normal((rows, heads), dtype=np.float32)
+
+    kv = _kv_rows(to_e4m3fn_bytes(k_f), scales)
+    if poison_unused:
+        used = bt[bt >= 0]
+        _poison_rows(kv, used)
+    return Workload(name=name, q=to_e4m3fn_bytes(q_f), kv_cache=kv,
+                    weights=np.ascontiguousarray(weights, dtype=np.float32),
+                    context_lens=ctx, block_tables=bt, max_model_len=int(max_model_len),
+                    next_n=int(next_n), k=int(k),
+                    meta={"table": table, "pool": int(pool)})
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads.
+# ---------------------------------------------------------------------------
+CONFIG_NAMES = {
+    1: "decode bs=1 N=1 H=32 ctx=2049 L=4096 identity table (reproducer shape)",
+    2: "decode bs=64 N=1 H=64 ctx~U[1,8192] L=8192 permuted 600k-row pool",
+    3: "MTP verify bs=32 N=2 H=64 ctx~U[2048,32768] L=32768 permuted pool",
+    4: "long context bs=4 N=1 H=64 ctx={65536,131071,131072,202752} L=202752 540k pool, 1% x8 keys",
+    5: "mixed serving bs=128 N=4 H=32 ctx~lognormal(6000,1.2) L=202752 interleaved pool",
+}
+
+
+def make_config(n: int, *, poison_unused: bool = True, seed: int | None = None) -> Workload:
+    rng = np.random.Generator(np.random.PCG64(42 + (n - 1) if seed is None else seed))
+    name = f"config{n}: {CONFIG_NAMES[n]}"
+    if n == 1:
+        ctx = np.array([2049])
+        return build(name, rng, batch=1, next_n=1, heads=32, ctx=ctx, max_model_len=4096,
+                     pool=2065, table="identity", table_width=2065, poison_unused=poison_unused)
+    if n == 2:
+        ctx = rng.integers(1, 8192, size=64, endpoint=True)
+        ctx[:5] = [2047, 2048, 2049, 4096, 4097]
+        return build(name, rng, batch=64, next_n=1, heads=64, ctx=ctx, max_model_len=8192,
+                     pool=600_000, table="permuted", table_width=8192,
+                     poison_unused=poison_unused)
+    if n == 3:
+        ctx = rng.integers(2048, 32768, size=32, endpoint=True)
+        return build(name, rng, batch=32, next_n=2, heads=64, ctx=ctx, max_model_len=32768,
+                     pool=int(ctx.sum()), table="permuted", table_width=32768,
+                     poison_unused=poison_unused)
+    if n == 4:
+        ctx = np.array([65536, 131071, 131072, 202752])
+        return build(name, rng, batch=4, next_n=1, heads=64, ctx=ctx, max_model_len=202752,
+                     pool=540_000, table="permuted", table_width=202752, outlier_frac=0.01,
+                     poison_unused=poison_unused)
+    if n == 5:
+        ctx = np.clip(np.round(np.exp(rng.normal(np.log(6000.0), 1.2, size=128))), 4, 202752)
+        ctx = ctx.astype(np.int64)
+        return build(name, rng, batch=128, next_n=4, heads=32, ctx=ctx, max_model_len=202752,
+                     pool=int(ctx.sum()), table="interleaved", table_width=int(ctx.max()),
+                     poison_unused=poison_unused)
+    raise ValueError(n)
+
+
+def make_case(*, batch, next_n, heads, ctx, max_model_len=None, seed=0, table="permuted",
+              pool=None, table_width=None, poison_unused=True, k=TOPK, **kw) -> Workload:
+    """A small seeded case (for sweeps and edge cases)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ctx = np.broadcast_to(np.asarray(ctx, dtype=np.int64), (batch,)).copy()
+    L = int(max_model_len or max(1, int(ctx.max(initial=1))))
+    if pool is None:
+        pool = int(ctx.max(initial=1)) if table == "identity" else max(1, int(ctx.sum()))
+    return build(f"case b{batch} n{next_n} h{heads} seed{seed}", rng, batch=batch,
+                 next_n=next_n, heads=heads, ctx=ctx, max_model_len=L, pool=pool, table=table,
+                 table_width=table_width, poison_unused=poison_unused, k=k, **kw)
+
+
+def page_random_bytes_case(ctx_len: int, seed: int = 42, heads: int = 32,
+                           max_model_len: int = 202752) -> Workload:
+    """The reproducer's own recipe: every cache byte uniform random (so keys
+    include NaN codes and the scales are arbitrary fp32 bit patterns), q ~ N(0,1)
+    cast to e4m3fn, weights ~ N(0,1), identity table of ctx + 16 blocks."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    blocks = ctx_len + 16
+    kv = rng.integers(0, 256, size=(blocks, ROW_BYTES), dtype=np.uint8)
+    q = to_e4m3fn_bytes(rng.standard_normal((1, 1, heads, HEAD_DIM), dtype=np.float32))
+    w = rng.standard_normal((1, heads), dtype=np.float32)
+    bt = np.arange(blocks, dtype=np.int32)[None, :]
+    return Workload(name=f"random-bytes ctx={ctx_len}", q=q, kv_cache=kv, weights=w,
+                    context_lens=np.array([ctx_len], dtype=np.int32), block_tables=bt,
+                    max_model_len=max_model_len, next_n=1)

@@ -1,0 +1,192 @@
+"""CPU oracle for the fp8 paged MQA logits and the per-row top-k that follows them.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The product path
+(the HIP library under ``fp8_paged_mqa_amd/`` and its binding) never calls it,
+and this module imports nothing from the product path.
+
+What it computes, and where that is defined
+-------------------------------------------
+Source page: the stepcodex.com issue mirror "[Bug] aiter ops triton attention
+pa_mqa_logits" (stepcodex.com/en/issue/bug-aiter-ops-triton-attention-pa),
+section "Minimal reproduction": the torch reference function (``torch_ref``)
+and the reproducer's ``test()``.
+
+* The KV cache row of a token holds D fp8-e4m3fn bytes followed by 4 bytes that
+  are read as one fp32 dequant scale. The row is dequantised as fp8 value times
+  scale before the dot product.
+* All H query heads of a decode row are dotted with the same dequantised key
+  (MQA: the cache has one key head).
+* Decode row j of request b sits at position ctx - N + j, where ctx is the
+  request's context length and N = next_n; token t is visible to it iff
+  t < ctx and t <= ctx - N + j. Every other slot of the output row is -inf.
+* logit = sum over heads of weight[row, h] * relu(score_h), row = b*N + j.
+* The reproducer keeps k = min(2048, ctx) positions per row with ``torch.topk``
+  and compares the two selections as sets (indices sorted before comparing).
+
+Precision: the page's text calls the reference "bf16", yet its code upcasts to
+fp32. This oracle reads the method as its exact mathematical definition and
+evaluates it in float64:
+
+* every finite e4m3fn value is an integer multiple of 2**-9 with magnitude
+  below 2**18, so a 128-term dot product of two such vectors is a multiple of
+  2**-18 below 2**43 in magnitude: exact in float64 whatever the summation
+  order (the matmul below is therefore exact);
+* the scale product, the relu, the weight product and the head sum are then
+  rounded once each in float64.
+
+Top-k: the row's visible positions are ordered by (logit descending, position
+ascending), with -0.0 equal to +0.0 (float comparison already treats them as
+equal), and the first min(k, visible) positions are kept. The page leaves the
+order of equal logits open; lowest-position-first is the reading taken here.
+
+No blocking, fusion or reordering beyond these steps is done.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+HEAD_DIM = 128          # index_head_dim of the models the page names (D)
+ROW_BYTES = HEAD_DIM + 4  # D fp8 bytes, then one little-endian fp32 scale
+
+
+# ---------------------------------------------------------------------------
+# Step 1: e4m3fn decode.
+# The page's reference views the cache bytes as torch.float8_e4m3fn. That
+# dtype is the OCP 8-bit floating point E4M3 format: 1 sign bit, 4 exponent
+# bits (bias 7), 3 mantissa bits, no infinities, S.1111.111 is NaN, exponent
+# field 0 encodes subnormals m * 2**-9.
+# ---------------------------------------------------------------------------
+def decode_e4m3fn(code: int) -> float:
+    """Value of one e4m3fn byte, from the format definition."""
+    code = int(code) & 0xFF
+    sign = -1.0 if (code >> 7) else 1.0
+    exponent = (code >> 3) & 0xF
+    mantissa = code & 0x7
+    if exponent == 0xF and mantissa == 0x7:
+        return math.nan
+    if exponent == 0:
+        return sign * mantissa * 2.0 ** -9          # (m / 8) * 2**(1 - 7)
+    return sign * (8 + mantissa) * 2.0 ** (exponent - 10)  # (1 + m/8) * 2**(e - 7)
+
+
+E4M3FN_VALUES = np.array([decode_e4m3fn(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_bytes(codes: np.ndarray) -> np.ndarray:
+    """Elementwise e4m3fn decode of a uint8 array into float64."""
+    return E4M3FN_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
+# ---------------------------------------------------------------------------
+# Step 2: the cache row. Bytes [0, D) are fp8 key values, bytes [D, D+4) are
+# the per-token fp32 scale, read little-endian (``.view(torch.float32)`` of the
+# trailing bytes in the page's reference). block_size is 1: one row per block.
+# ---------------------------------------------------------------------------
+def split_kv_rows(kv_cache: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Returns (key values [num_blocks, D] float64, scales [num_blocks] float64)."""
+    kv = np.asarray(kv_cache, dtype=np.uint8).reshape(-1, ROW_BYTES)
+    keys = decode_bytes(kv[:, :HEAD_DIM])
+    scales = np.ascontiguousarray(kv[:, HEAD_DIM:ROW_BYTES]).view("<f4")[:, 0]
+    return keys, scales.astype(np.float64)
+
+
+def visible_count(ctx: int, next_n: int, j: int, max_model_len: int) -> int:
+    """Number of visible positions of decode row j: t <= ctx - N + j (and t < ctx,
+    which that already implies), capped by the output row length."""
+    return max(0, min(ctx - next_n + j + 1, max_model_len))
+
+
+def _check_preconditions(context_lens, block_tables, max_model_len):
+    for b, ctx in enumerate(np.asarray(context_lens).tolist()):
+        if ctx < 0 or ctx > max_model_len or ctx > block_tables.shape[1]:
+            raise ValueError(
+                f"request {b}: context length {ctx} outside [0, min(max_model_len, table width)]")
+
+
+# ---------------------------------------------------------------------------
+# Steps 3-5: scores, relu, weights, head sum, mask.
+# ---------------------------------------------------------------------------
+def paged_mqa_logits(q, kv_cache, weights, context_lens, block_tables, max_model_len):
+    """Logits [B*N, max_model_len] float64.
+
+    q            uint8 [B, N, H, D]   e4m3fn bytes
+    kv_cache     uint8 [num_blocks, D + 4] (block_size 1)
+    weights      float [B*N, H]
+    context_lens int   [B]
+    block_tables int   [B, W]         physical row of logical token t
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    B, N, H, D = q.shape
+    assert D == HEAD_DIM
+    block_tables = np.asarray(block_tables)
+    _check_preconditions(context_lens, block_tables, max_model_len)
+    keys, scales = split_kv_rows(kv_cache)
+    w = np.asarray(weights, dtype=np.float64).reshape(B * N, H)
+    qv = decode_bytes(q)                                   # [B, N, H, D]
+    out = np.full((B * N, max_model_len), -np.inf, dtype=np.float64)
+    for b in range(B):
+        ctx = int(context_lens[b])
+        if ctx <= 0:
+            continue
+        phys = block_tables[b, :ctx].astype(np.int64)
+        k_b = keys[phys]                                   # [ctx, D]  key of token t
+        s_b = scales[phys]                                 # [ctx]
+        for j in range(N):
+            nv = visible_count(ctx, N, j, max_model_len)
+            if nv == 0:
+                continue
+            score = k_b[:nv] @ qv[b, j].T                  # [nv, H]  q_h . k_t, exact
+            x = score * s_b[:nv, None]                     # dequant scale on the key
+            out[b * N + j, :nv] = np.maximum(x, 0.0) @ w[b * N + j]   # sum_h w_h relu(x_h)
+    return out
+
+
+def paged_mqa_logit_at(q, kv_cache, weights, context_lens, block_tables, max_model_len, row, t):
+    """One logit, computed on its own with plain loops (for sampled checks at
+    sizes where the whole output is not wanted)."""
+    q = np.asarray(q, dtype=np.uint8)
+    B, N, H, D = q.shape
+    b, j = divmod(int(row), N)
+    ctx = int(context_lens[b])
+    if t < 0 or t >= visible_count(ctx, N, j, max_model_len):
+        return -math.inf
+    kv = np.asarray(kv_cache, dtype=np.uint8).reshape(-1, ROW_BYTES)
+    phys = int(block_tables[b, t])
+    key = decode_bytes(kv[phys, :HEAD_DIM])
+    scale = float(np.ascontiguousarray(kv[phys, HEAD_DIM:ROW_BYTES]).view("<f4")[0])
+    w = np.asarray(weights, dtype=np.float64).reshape(B * N, H)[row]
+    total = 0.0
+    for h in range(H):
+        score = float(np.dot(decode_bytes(q[b, j, h]), key))
+        total += float(w[h]) * max(score * scale, 0.0)
+    return total
+
+
+# ---------------------------------------------------------------------------
+# Step 6: per-row top-k.
+# ---------------------------------------------------------------------------
+def topk_row(values: np.ndarray, k: int) -> np.ndarray:
+    """Positions of the k largest entries of ``values`` (all of them if fewer),
+    ties broken by lowest position, returned sorted ascending."""
+    values = np.asarray(values, dtype=np.float64)
+    order = np.lexsort((np.arange(values.size), -values))   # last key is primary
+    return np.sort(order[:min(k, values.size)])
+
+
+def topk(logits, context_lens, next_n, k, max_model_len=None):
+    """Indices [B*N, k] int32. Row r keeps min(k, visible_r) positions of its
+    visible prefix (ascending), then -1 padding."""
+    logits = np.asarray(logits)
+    rows, L = logits.shape
+    if max_model_len is None:
+        max_model_len = L
+    out = np.full((rows, k), -1, dtype=np.int32)
+    for r in range(rows):
+        b, j = divmod(r, next_n)
+        nv = visible_count(int(context_lens[b]), next_n, j, max_model_len)
+        sel = topk_row(logits[r, :nv], k)
+        out[r, :sel.size] = sel
+    return out

@@ -1,0 +1,73 @@
+"""Plants plausible mistakes in copies of the oracle (on the CPU) and requires
+the pins to catch every one of them: evidence that the pins constrain each
+step of the oracle, not just its overall shape."""
+import importlib.util
+import os
+import types
+
+import pytest
+
+from pins import PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "mqa_oracle.py")
+
+# (description, text in the oracle, replacement)
+MUTANTS = [
+    ("exponent bias 8", "2.0 ** (exponent - 10)", "2.0 ** (exponent - 11)"),
+    ("subnormal step 2^-10", "mantissa * 2.0 ** -9", "mantissa * 2.0 ** -10"),
+    ("fnuz-style NaN at 0x80", "if exponent == 0xF and mantissa == 0x7:",
+     "if code == 0x80:"),
+    ("sign bit ignored", "sign = -1.0 if (code >> 7) else 1.0", "sign = 1.0"),
+    ("scale read big-endian", '"<f4"', '">f4"'),
+    ("scale not applied", "x = score * s_b[:nv, None]", "x = score"),
+    ("relu after the head sum", "np.maximum(x, 0.0) @ w[b * N + j]", "np.maximum(x @ w[b * N + j], 0.0)"),
+    ("no relu", "np.maximum(x, 0.0) @ w[b * N + j]", "x @ w[b * N + j]"),
+    ("causal window one short", "ctx - next_n + j + 1, max_model_len", "ctx - next_n + j, max_model_len"),
+    ("causal window one long", "ctx - next_n + j + 1, max_model_len", "ctx - next_n + j + 2, max_model_len"),
+    ("next_n offset ignored", "ctx - next_n + j + 1, max_model_len", "ctx, max_model_len"),
+    ("weights of row b*N", "@ w[b * N + j]", "@ w[b * N]"),
+    ("block table ignored", "phys = block_tables[b, :ctx].astype(np.int64)",
+     "phys = np.arange(ctx, dtype=np.int64)"),
+    ("query of decode row 0 for every row", "score = k_b[:nv] @ qv[b, j].T", "score = k_b[:nv] @ qv[b, 0].T"),
+    ("query head/dim transposed", "score = k_b[:nv] @ qv[b, j].T",
+     "score = k_b[:nv, :qv.shape[2]] @ qv[b, j][:, :qv.shape[2]]"),
+    ("top-k keeps the smallest", "order = np.lexsort((np.arange(values.size), -values))",
+     "order = np.lexsort((np.arange(values.size), values))"),
+    ("top-k ties to highest position", "order = np.lexsort((np.arange(values.size), -values))",
+     "order = np.lexsort((-np.arange(values.size), -values))"),
+    ("top-k one short", "return np.sort(order[:min(k, values.size)])",
+     "return np.sort(order[:min(k, values.size) - 1])"),
+]
+
+
+def _load_mutant(old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert old in text, f"mutation site not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = SRC
+    exec(compile(text.replace(old, new), SRC + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+def _caught(mod):
+    for pin in PINS:
+        try:
+            pin(mod)
+        except Exception:   # an assertion, or the mutant crashing on a pin's input
+            return pin.__name__
+    return None
+
+
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(desc, old, new):
+    assert _caught(_load_mutant(old, new)) is not None, f"no pin catches: {desc}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    with open(SRC) as f:
+        text = f.read()
+    mod = types.ModuleType("oracle_copy")
+    exec(compile(text, SRC, "exec"), mod.__dict__)
+    assert _caught(mod) is None

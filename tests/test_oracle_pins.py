@@ -1,0 +1,10 @@
+"""The CPU oracle against facts outside itself (CPU only)."""
+import pytest
+
+import oracle
+from pins import PINS
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle.mqa_oracle)
