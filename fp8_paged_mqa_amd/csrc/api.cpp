@@ -1,0 +1,107 @@
+// C ABI of libmqa: argument validation on the host, then kernel launches on the
+// caller's stream. Declarations and the contract of each entry point: include/mqa.h.
+#include "mqa.h"
+
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int32_t kHeadDim = 128;
+constexpr int32_t kMaxTopk = 2048;
+constexpr int32_t kMaxModelLen = 1 << 30;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape checks shared by both entry points. Sizes that cannot describe a problem are
+// MQA_ERR_SHAPE; well-formed shapes the kernels do not implement are MQA_ERR_UNSUPPORTED.
+int check_shape(const mqa_shape* s, int32_t max_model_len) {
+  if (s == nullptr) return MQA_ERR_NULL;
+  if (s->batch < 0 || s->next_n < 1 || s->heads < 1 || s->head_dim < 1 || s->block_size < 1 ||
+      s->block_table_stride < 1 || s->num_blocks < 1 || max_model_len < 1)
+    return MQA_ERR_SHAPE;
+  if ((int64_t)s->batch * s->next_n > INT32_MAX) return MQA_ERR_SHAPE;
+  if (s->head_dim != kHeadDim || s->block_size != 1) return MQA_ERR_UNSUPPORTED;
+  if (s->heads % 16 != 0 || s->heads > 128) return MQA_ERR_UNSUPPORTED;
+  if (s->next_n > 4) return MQA_ERR_UNSUPPORTED;
+  if (max_model_len > kMaxModelLen) return MQA_ERR_UNSUPPORTED;
+  return MQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mqa_status_string(int status) {
+  switch (status) {
+    case MQA_OK: return "ok";
+    case MQA_ERR_NULL: return "a required pointer is NULL";
+    case MQA_ERR_SHAPE: return "invalid shape or size";
+    case MQA_ERR_UNSUPPORTED:
+      return "unsupported: needs head_dim 128, block_size 1, heads a multiple of 16 up to 128, "
+             "next_n 1..4, max_model_len <= 2^30, k 1..2048, 16-byte aligned q and weights, "
+             "4-byte aligned kv_cache, logits, idx and integer arrays";
+    case MQA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MQA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* weights,
+                     const int32_t* context_lens, const int32_t* block_tables,
+                     int32_t max_model_len, float* out, const mqa_shape* shape,
+                     hipStream_t stream) {
+  const int st = check_shape(shape, max_model_len);
+  if (st != MQA_OK) return st;
+  if (shape->batch == 0) return MQA_OK;
+  if (!q || !kv_cache || !weights || !context_lens || !block_tables || !out) return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(weights, 16) || !aligned(kv_cache, 4) || !aligned(out, 4) ||
+      !aligned(context_lens, 4) || !aligned(block_tables, 4))
+    return MQA_ERR_UNSUPPORTED;
+  mqa::LogitsLaunch a;
+  a.q = q;
+  a.kv = kv_cache;
+  a.w = weights;
+  a.ctx_lens = context_lens;
+  a.bt = block_tables;
+  a.out = out;
+  a.num_blocks = shape->num_blocks;
+  a.batch = shape->batch;
+  a.next_n = shape->next_n;
+  a.heads = shape->heads;
+  a.bt_stride = shape->block_table_stride;
+  a.max_model_len = max_model_len;
+  return mqa::launch_logits(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+size_t mqa_topk_workspace_bytes(const mqa_shape* shape, int32_t max_model_len, int32_t k) {
+  if (check_shape(shape, max_model_len) != MQA_OK || k < 1 || k > kMaxTopk) return 0;
+  return 0;  // the single-pass-per-row kernel keeps all of its state in LDS
+}
+
+int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model_len, int32_t k,
+             int32_t* idx, const mqa_shape* shape, void* workspace, size_t workspace_bytes,
+             hipStream_t stream) {
+  const int st = check_shape(shape, max_model_len);
+  if (st != MQA_OK) return st;
+  if (k < 1) return MQA_ERR_SHAPE;
+  if (k > kMaxTopk) return MQA_ERR_UNSUPPORTED;
+  const size_t need = mqa_topk_workspace_bytes(shape, max_model_len, k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MQA_ERR_WORKSPACE;
+  if (shape->batch == 0) return MQA_OK;
+  if (!logits || !context_lens || !idx) return MQA_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(context_lens, 4) || !aligned(idx, 4)) return MQA_ERR_UNSUPPORTED;
+  mqa::TopkLaunch a;
+  a.logits = logits;
+  a.ctx_lens = context_lens;
+  a.idx = idx;
+  a.batch = shape->batch;
+  a.next_n = shape->next_n;
+  a.bt_stride = shape->block_table_stride;
+  a.max_model_len = max_model_len;
+  a.k = k;
+  return mqa::launch_topk(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel translation units.
+// Validation happens in api.cpp; the launchers assume valid arguments.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace mqa {
+
+struct LogitsLaunch {
+  const uint8_t* q;
+  const uint8_t* kv;
+  const float* w;
+  const int32_t* ctx_lens;
+  const int32_t* bt;
+  float* out;
+  int64_t num_blocks;
+  int32_t batch, next_n, heads, bt_stride, max_model_len;
+};
+
+struct TopkLaunch {
+  const float* logits;
+  const int32_t* ctx_lens;
+  int32_t* idx;
+  int32_t batch, next_n, bt_stride, max_model_len, k;
+};
+
+// Enqueue the logits kernel on `stream`; returns the hipError_t of the launch.
+hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream);
+
+// Enqueue the top-k kernel(s) on `stream`.
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
+
+}  // namespace mqa

@@ -1,0 +1,132 @@
+"""ctypes binding of libmqa's C ABI (include/mqa.h), same entry-point names.
+
+Argument marshalling only: tensors are passed as device pointers, shapes as an
+``mqa_shape`` struct, and the current torch stream as the HIP stream. Every step
+of the computation runs in libmqa's kernels. Importing this module loads the
+library and raises if it has not been built (``python -m fp8_paged_mqa_amd.build``);
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa.so")
+
+MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED, MQA_ERR_WORKSPACE, MQA_ERR_HIP = range(6)
+
+EXPORTS = ("mqa_paged_logits", "mqa_topk", "mqa_topk_workspace_bytes", "mqa_status_string")
+
+
+class mqa_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("next_n", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("block_table_stride", ctypes.c_int32), ("num_blocks", ctypes.c_int64)]
+
+
+class MqaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({mqa_status_string(status)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fp8_paged_mqa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    shp = ctypes.POINTER(mqa_shape)
+    lib.mqa_paged_logits.argtypes = [vp, vp, vp, vp, vp, i32, vp, shp, vp]
+    lib.mqa_paged_logits.restype = ctypes.c_int
+    lib.mqa_topk.argtypes = [vp, vp, i32, i32, vp, shp, vp, sz, vp]
+    lib.mqa_topk.restype = ctypes.c_int
+    lib.mqa_topk_workspace_bytes.argtypes = [shp, i32, i32]
+    lib.mqa_topk_workspace_bytes.restype = sz
+    lib.mqa_status_string.argtypes = [ctypes.c_int]
+    lib.mqa_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def make_shape(batch, next_n, heads, num_blocks, block_table_stride, head_dim=128, block_size=1):
+    return mqa_shape(int(batch), int(next_n), int(heads), int(head_dim), int(block_size),
+                     int(block_table_stride), int(num_blocks))
+
+
+def shape_of(q: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tensor) -> mqa_shape:
+    """Shape struct from tensors laid out as the header describes: q [B,N,H,D],
+    kv_cache [num_blocks, (block_size, 1,) D+4], block_tables [B, W]."""
+    B, N, H, D = q.shape
+    return make_shape(B, N, H, kv_cache.shape[0], block_tables.shape[1], head_dim=D,
+                      block_size=kv_cache.shape[1] if kv_cache.dim() == 4 else 1)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def mqa_status_string(status: int) -> str:
+    return _lib.mqa_status_string(int(status)).decode()
+
+
+def mqa_paged_logits(q, kv_cache, weights, context_lens, block_tables, max_model_len, out,
+                     shape: mqa_shape | None = None, stream=None, check: bool = True) -> int:
+    """out[B*N, L] <- indexer logits. Tensors must be contiguous device tensors:
+    q uint8 [B,N,H,128], kv_cache uint8 [num_blocks,132], weights f32 [B*N,H],
+    context_lens i32 [B], block_tables i32 [B,W], out f32 [B*N,L]."""
+    if shape is None:
+        shape = shape_of(q, kv_cache, block_tables)
+    st = _lib.mqa_paged_logits(_ptr(q), _ptr(kv_cache), _ptr(weights), _ptr(context_lens),
+                               _ptr(block_tables), int(max_model_len), _ptr(out),
+                               ctypes.byref(shape), _stream(stream))
+    if check and st != MQA_OK:
+        raise MqaError(st, "mqa_paged_logits")
+    return st
+
+
+def mqa_topk_workspace_bytes(shape: mqa_shape, max_model_len: int, k: int) -> int:
+    return int(_lib.mqa_topk_workspace_bytes(ctypes.byref(shape), int(max_model_len), int(k)))
+
+
+def mqa_topk(logits, context_lens, max_model_len, k, idx, shape: mqa_shape, workspace=None,
+             stream=None, check: bool = True) -> int:
+    """idx[B*N, k] <- per-row top-k positions (a set per row, -1 padded)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.mqa_topk(_ptr(logits), _ptr(context_lens), int(max_model_len), int(k), _ptr(idx),
+                       ctypes.byref(shape), _ptr(workspace), ws_bytes, _stream(stream))
+    if check and st != MQA_OK:
+        raise MqaError(st, "mqa_topk")
+    return st
+
+
+class Indexer:
+    """Holds the device buffers of one problem shape (output, indices, top-k
+    workspace) so that repeated calls allocate nothing."""
+
+    def __init__(self, batch, next_n, heads, num_blocks, block_table_stride, max_model_len,
+                 k=2048, device="cuda"):
+        self.shape = make_shape(batch, next_n, heads, num_blocks, block_table_stride)
+        self.max_model_len = int(max_model_len)
+        self.k = int(k)
+        rows = batch * next_n
+        self.logits = torch.empty((rows, self.max_model_len), dtype=torch.float32, device=device)
+        self.idx = torch.empty((rows, self.k), dtype=torch.int32, device=device)
+        nbytes = mqa_topk_workspace_bytes(self.shape, self.max_model_len, self.k)
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+    def __call__(self, q, kv_cache, weights, context_lens, block_tables, stream=None):
+        mqa_paged_logits(q, kv_cache, weights, context_lens, block_tables, self.max_model_len,
+                         self.logits, self.shape, stream)
+        mqa_topk(self.logits, context_lens, self.max_model_len, self.k, self.idx, self.shape,
+                 self.workspace, stream)
+        return self.logits, self.idx

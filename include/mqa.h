@@ -1,0 +1,139 @@
+/*
+ * mqa.h - C ABI of libmqa: fp8 paged MQA logits and per-row top-k on MI355X (gfx950).
+ *
+ * The operation is the decode step of the sparse-attention indexer described on
+ * the stepcodex.com issue page "[Bug] aiter ops triton attention pa_mqa_logits"
+ * (section "Minimal reproduction": the torch reference function and the
+ * reproducer's top-k comparison; section "Observations while narrowing it down"
+ * for block_size 1 and the index head counts).
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer (hipMalloc or torch CUDA tensor memory),
+ *     except `shape`, which is a host pointer read during the call only.
+ *   - The caller owns all memory. The library never allocates, frees, synchronises,
+ *     or reads device memory from the host. All work is enqueued on `stream`
+ *     (0 = the default stream), so calls are asynchronous and capturable into a
+ *     HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued. A rejected
+ *     call returns a nonzero status and enqueues nothing. MQA_ERR_HIP reports a
+ *     launch failure seen by hipGetLastError after the launch.
+ *   - Values that live on the device (context lengths, block-table entries) cannot
+ *     be checked on the host. The kernels clamp them so that no access leaves the
+ *     buffers described by `shape`:
+ *       ctx is read as min(max(ctx, 0), block_table_stride, max_model_len);
+ *       a block-table entry outside [0, num_blocks) yields NaN logits for that
+ *       token instead of a memory access.
+ *   - Calls are reentrant: no mutable global state.
+ */
+#ifndef MQA_H
+#define MQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  MQA_OK = 0,
+  MQA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MQA_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be, or overflows */
+  MQA_ERR_UNSUPPORTED = 3, /* a valid shape outside the supported domain (below) */
+  MQA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than mqa_topk_workspace_bytes */
+  MQA_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * Problem shape (host struct).
+ *   batch               B, number of requests (>= 0; 0 enqueues nothing)
+ *   next_n              N, decode rows per request (speculative depth + 1), 1..4
+ *   heads               H, index query heads, a multiple of 16 in [16, 128]
+ *   head_dim            D, must be 128
+ *   block_size          tokens per KV block, must be 1
+ *   block_table_stride  W, int32 elements per block-table row (>= 1)
+ *   num_blocks          physical rows in the KV cache (>= 1)
+ * Row r of the logits and of the indices is decode row j of request b, r = b*N + j.
+ */
+typedef struct mqa_shape {
+  int32_t batch;
+  int32_t next_n;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t block_table_stride;
+  int64_t num_blocks;
+} mqa_shape;
+
+/*
+ * mqa_paged_logits - indexer logits for every decode row and every position.
+ *
+ * Definition (stepcodex.com pa_mqa_logits issue, "Minimal reproduction", the torch
+ * reference): for row r = b*N + j with context length ctx = context_lens[b], position t
+ * is visible iff t <= ctx - N + j (the row's own position; it implies t < ctx). For a
+ * visible t with physical row p = block_tables[b*W + t]:
+ *     k      = e4m3fn bytes kv_cache[p*132 + 0 .. 127]          (OCP E4M3, bias 7)
+ *     scale  = little-endian fp32 at kv_cache[p*132 + 128 .. 131]
+ *     out[r*max_model_len + t] = sum_h weights[r*H + h] * relu(scale * (q[b,j,h,:] . k))
+ * Every other slot of the row, t in [visible, max_model_len), is written with -inf.
+ *
+ *   q               uint8  [B, N, H, 128]   e4m3fn, contiguous
+ *   kv_cache        uint8  [num_blocks, 132] 128 e4m3fn key bytes, then the fp32 scale;
+ *                                            rows are 4-byte aligned (pointer must be too)
+ *   weights         float  [B*N, H]
+ *   context_lens    int32  [B]
+ *   block_tables    int32  [B, W]
+ *   max_model_len   L >= 1, the length of each output row
+ *   out             float  [B*N, L]         every element is written
+ *   shape, stream   see above
+ * Accuracy: fp8 x fp8 products are exact, accumulated in fp32; relu, weight and head
+ * sum in fp32. Results agree with the exact definition to 5e-3 + 1e-3*|logit| on the
+ * supported distributions; NaN key codes or NaN/Inf scales propagate as NaN.
+ * Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED or MQA_ERR_HIP.
+ */
+int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* weights,
+                     const int32_t* context_lens, const int32_t* block_tables,
+                     int32_t max_model_len, float* out, const mqa_shape* shape,
+                     hipStream_t stream);
+
+/*
+ * mqa_topk - positions of the k largest logits of each row's visible prefix.
+ *
+ * Definition (stepcodex.com pa_mqa_logits issue, "Minimal reproduction": the reproducer
+ * keeps k = min(2048, ctx) positions per row with topk and compares them as sets): row r
+ * has visible = max(0, min(ctx - N + j + 1, L)) positions. The call writes
+ * idx[r*k + 0 .. m-1], m = min(k, visible), with the m positions t < visible whose
+ * logits are largest, in unspecified order (a set), and idx[r*k + m .. k-1] = -1.
+ * Order: larger logit first; equal logits (-0.0 equals +0.0) by lower position first.
+ * NaN logits are ordered by their bit patterns (positive NaN above +inf).
+ *
+ *   logits          float  [B*N, L]   as written by mqa_paged_logits (only the visible
+ *                                     prefix of each row is read)
+ *   context_lens    int32  [B]
+ *   max_model_len   L, the row stride of logits
+ *   k               1 .. 2048
+ *   idx             int32  [B*N, k]
+ *   workspace       device scratch of at least mqa_topk_workspace_bytes(shape,
+ *                   max_model_len, k) bytes; contents on entry do not matter, the
+ *                   call initialises what it uses, in stream order
+ * Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED,
+ * MQA_ERR_WORKSPACE or MQA_ERR_HIP.
+ */
+int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model_len,
+             int32_t k, int32_t* idx, const mqa_shape* shape, void* workspace,
+             size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace size for mqa_topk with this shape, L and k (0 when the shape is invalid). */
+size_t mqa_topk_workspace_bytes(const mqa_shape* shape, int32_t max_model_len, int32_t k);
+
+/* Static description of a status code (never NULL). */
+const char* mqa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQA_H */

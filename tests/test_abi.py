@@ -1,0 +1,122 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp8_paged_mqa_amd import mqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mqa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mqa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(mqa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", mqa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(mqa._lib, name)
+
+
+def test_status_strings():
+    for st in range(6):
+        assert mqa.mqa_status_string(st)
+    assert mqa.mqa_status_string(0) == "ok"
+    assert "unknown" in mqa.mqa_status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every case below is rejected first
+
+
+def call_logits(shape, L=100, ptrs=(FAKE,) * 6):
+    q, kv, w, ctx, bt, out = ptrs
+    return mqa._lib.mqa_paged_logits(q, kv, w, ctx, bt, L, out,
+                                     ctypes.byref(shape) if shape is not None else None, None)
+
+
+def call_topk(shape, L=100, k=2048, ws=None, ws_bytes=0, ptrs=(FAKE,) * 3):
+    logits, ctx, idx = ptrs
+    return mqa._lib.mqa_topk(logits, ctx, L, k, idx,
+                             ctypes.byref(shape) if shape is not None else None, ws, ws_bytes, None)
+
+
+def good_shape(**kw):
+    d = dict(batch=2, next_n=2, heads=64, num_blocks=1000, block_table_stride=100)
+    d.update(kw)
+    return mqa.make_shape(**d)
+
+
+@pytest.mark.parametrize("kw,L,status", [
+    (dict(batch=-1), 100, mqa.MQA_ERR_SHAPE),
+    (dict(next_n=0), 100, mqa.MQA_ERR_SHAPE),
+    (dict(heads=0), 100, mqa.MQA_ERR_SHAPE),
+    (dict(num_blocks=0), 100, mqa.MQA_ERR_SHAPE),
+    (dict(block_table_stride=0), 100, mqa.MQA_ERR_SHAPE),
+    ({}, 0, mqa.MQA_ERR_SHAPE),
+    (dict(head_dim=64), 100, mqa.MQA_ERR_UNSUPPORTED),
+    (dict(block_size=16), 100, mqa.MQA_ERR_UNSUPPORTED),   # the page's block sizes 16/64/256
+    (dict(block_size=64), 100, mqa.MQA_ERR_UNSUPPORTED),
+    (dict(block_size=256), 100, mqa.MQA_ERR_UNSUPPORTED),
+    (dict(heads=24), 100, mqa.MQA_ERR_UNSUPPORTED),
+    (dict(heads=144), 100, mqa.MQA_ERR_UNSUPPORTED),
+    (dict(next_n=5), 100, mqa.MQA_ERR_UNSUPPORTED),
+    ({}, (1 << 30) + 1, mqa.MQA_ERR_UNSUPPORTED),
+])
+def test_logits_rejects_bad_shapes(kw, L, status):
+    assert call_logits(good_shape(**kw), L=L) == status
+    assert call_topk(good_shape(**kw), L=L) == status
+
+
+def test_null_pointers():
+    assert call_logits(None) == mqa.MQA_ERR_NULL
+    assert call_topk(None) == mqa.MQA_ERR_NULL
+    for i in range(6):
+        ptrs = [FAKE] * 6
+        ptrs[i] = None
+        assert call_logits(good_shape(), ptrs=tuple(ptrs)) == mqa.MQA_ERR_NULL, i
+    for i in range(3):
+        ptrs = [FAKE] * 3
+        ptrs[i] = None
+        assert call_topk(good_shape(), ptrs=tuple(ptrs)) == mqa.MQA_ERR_NULL, i
+
+
+def test_misaligned_pointers():
+    odd = ctypes.c_void_p(0x10002)
+    for i in range(6):
+        ptrs = [FAKE] * 6
+        ptrs[i] = odd
+        assert call_logits(good_shape(), ptrs=tuple(ptrs)) == mqa.MQA_ERR_UNSUPPORTED, i
+    q_off = ctypes.c_void_p(0x10004)   # 4-byte aligned but not 16: q and weights need 16
+    assert call_logits(good_shape(), ptrs=(q_off,) + (FAKE,) * 5) == mqa.MQA_ERR_UNSUPPORTED
+    assert call_logits(good_shape(), ptrs=(FAKE, FAKE, q_off) + (FAKE,) * 3) == mqa.MQA_ERR_UNSUPPORTED
+
+
+def test_topk_k_range():
+    assert call_topk(good_shape(), k=0) == mqa.MQA_ERR_SHAPE
+    assert call_topk(good_shape(), k=2049) == mqa.MQA_ERR_UNSUPPORTED
+
+
+def test_empty_batch_is_a_no_op():
+    # batch 0 enqueues nothing, so null data pointers are fine and no GPU is touched
+    assert call_logits(good_shape(batch=0), ptrs=(None,) * 6) == mqa.MQA_OK
+    assert call_topk(good_shape(batch=0), ptrs=(None,) * 3) == mqa.MQA_OK
+
+
+def test_workspace_size_query():
+    assert mqa.mqa_topk_workspace_bytes(good_shape(), 100, 2048) >= 0
+    assert mqa.mqa_topk_workspace_bytes(good_shape(block_size=2), 100, 2048) == 0
+    assert mqa.mqa_topk_workspace_bytes(good_shape(), 100, 0) == 0
