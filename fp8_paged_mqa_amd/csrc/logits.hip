@@ -8,17 +8,23 @@
 // "[Bug] aiter ops triton attention pa_mqa_logits", section "Minimal reproduction".
 //
 // Mapping onto CDNA4
-//   * One wave owns a group of decode rows (JPG rows of H heads, at most 8 MFMA row tiles
-//     of 16 heads) and a contiguous token range. Its query rows stay in VGPRs for the
-//     whole range, in the A-operand layout of v_mfma_f32_16x16x128_f8f6f4 (one
-//     instruction spans D = 128).
-//   * Keys are gathered straight from HBM into the B-operand layout: lane (g, c), g = lane/16,
-//     c = lane%16, owns token c of a 16-token column tile and reads bytes [16g, 16g+16)
-//     and [64+16g, 64+16g+16) of that token's row, so each dwordx4 load instruction covers
-//     the first (then the second) 64 contiguous bytes of 16 rows. A and B use the same
-//     byte-to-k assignment, so the contraction is over all 128 k whatever order the
-//     hardware uses internally. No LDS round trip: the gathered bytes are already where
-//     the MFMA wants them.
+//   * Precision: gfx950's fp8 MFMAs (16x16x128 f8f6f4 and 16x16x32 fp8) round the dot
+//     product at about 2^-15.5 of sum|q_i k_i|, measured against exact products; near a
+//     cancelling head sum that exceeds the 5e-3 + 1e-3*|logit| budget. So fp8 bytes are
+//     converted exactly to f16 (v_cvt_scalef32_pk_f16_fp8, scale 1) and contracted with
+//     v_mfma_f32_16x16x32_f16, four chained per 128-wide row: f16 products of e4m3
+//     values are exact and the fp32 accumulation is correctly rounded.
+//   * One wave owns a group of decode rows (at most 4 MFMA row tiles of 16 heads, so
+//     at most 64 query rows for H <= 64) and a contiguous token range. Its query rows stay
+//     in VGPRs, already in f16, in the A-operand layout, for the whole range. Decode rows
+//     beyond one wave's share go to sibling waves of the workgroup that walk the same
+//     tokens (their second read of a key row hits L2).
+//   * Keys are gathered straight from HBM into the B-operand slots: lane (g, c),
+//     g = lane/16, c = lane%16, owns token c of a 16-token column tile and reads bytes
+//     [16g, 16g+16) and [64+16g, 64+16g+16) of that token's row, so each dwordx4 load
+//     instruction covers the first (then the second) 64 contiguous bytes of 16 rows. A
+//     and B use the same byte-to-k assignment, so the contraction covers all 128 k
+//     whatever order the hardware uses internally.
 //   * The block table is read 64 tokens at a time (one coalesced dword per lane) and
 //     redistributed with ds_bpermute; table reads run two 64-token stages ahead of use,
 //     key reads one stage ahead, so a wave keeps ~8 KB of gathers in flight.
@@ -38,8 +44,10 @@ namespace mqa {
 namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kD = 128;         // head_dim
 constexpr int kRow = kD + 4;    // cache row bytes: keys + fp32 scale
@@ -67,6 +75,33 @@ __device__ __forceinline__ i32x4 load16(const uint8_t* p) {
   return v;
 }
 
+// 8 e4m3fn bytes (two dwords) -> 8 f16 values, exactly (every e4m3fn value, NaN and
+// subnormals included, is representable in f16).
+__device__ __forceinline__ f16x8 fp8x8_to_f16(int lo, int hi) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)lo, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)lo, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)hi, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)hi, 1.0f, true);
+  const f16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const f16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// The 32 bytes a lane holds for one row (16 at 16g, 16 at 64+16g) as the four f16x8
+// operands of the chained k-steps.
+struct Operand {
+  f16x8 k[4];
+};
+
+__device__ __forceinline__ Operand to_operand(i32x4 lo, i32x4 hi) {
+  Operand o;
+  o.k[0] = fp8x8_to_f16(lo.x, lo.y);
+  o.k[1] = fp8x8_to_f16(lo.z, lo.w);
+  o.k[2] = fp8x8_to_f16(hi.x, hi.y);
+  o.k[3] = fp8x8_to_f16(hi.z, hi.w);
+  return o;
+}
+
 // Gathered keys of one 64-token stage, in the lane's B-operand slots.
 struct Stage {
   i32x4 lo[kTilesPerStage];
@@ -74,8 +109,10 @@ struct Stage {
   float scale[kTilesPerStage];
 };
 
+// Up to 4 row tiles fit two waves per SIMD (<= 256 VGPRs); the 5..8-tile variants
+// (H > 64) take the whole register file.
 template <int TPJ, int JPG>
-__global__ __launch_bounds__(256, 2) void paged_logits_kernel(Params p) {
+__global__ __launch_bounds__(256, (TPJ * JPG <= 4) ? 2 : 1) void paged_logits_kernel(Params p) {
   constexpr int TILES = TPJ * JPG;  // MFMA row tiles (16 heads each) held by one wave
   static_assert(TILES >= 1 && TILES <= 8, "query tile budget");
 
@@ -101,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void paged_logits_kernel(Params p) {
   const int64_t out_row0 = (int64_t)(b * p.N + j0) * p.L;
 
   // Query tiles (A operand) and the weights of the 4 heads each lane reduces per tile.
-  i32x8 qa[TILES];
+  Operand qa[TILES];
   f32x4 wv[TILES];
   {
     const uint8_t* qb = p.q + ((int64_t)b * p.N + j0) * p.H * kD;
@@ -112,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void paged_logits_kernel(Params p) {
       const uint8_t* qr = qb + (m * 16 + c) * kD;
       i32x4 a0 = live ? load16(qr + 16 * g) : i32x4{0, 0, 0, 0};
       i32x4 a1 = live ? load16(qr + 64 + 16 * g) : i32x4{0, 0, 0, 0};
-      qa[m] = i32x8{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      qa[m] = to_operand(a0, a1);
       wv[m] = live ? *reinterpret_cast<const f32x4*>(wb + m * 16 + 4 * g) : f32x4{0, 0, 0, 0};
     }
   }
@@ -159,14 +196,18 @@ __global__ __launch_bounds__(256, 2) void paged_logits_kernel(Params p) {
         if (tc + u * 16 >= t_need) break;  // wave-uniform
         const float sc = s.scale[u];
         const int flip = (__float_as_int(sc) < 0) ? (int)0x80808080 : 0;
-        const i32x8 kb = {s.lo[u].x ^ flip, s.lo[u].y ^ flip, s.lo[u].z ^ flip, s.lo[u].w ^ flip,
-                          s.hi[u].x ^ flip, s.hi[u].y ^ flip, s.hi[u].z ^ flip, s.hi[u].w ^ flip};
+        const i32x4 lo = {s.lo[u].x ^ flip, s.lo[u].y ^ flip, s.lo[u].z ^ flip, s.lo[u].w ^ flip};
+        const i32x4 hi = {s.hi[u].x ^ flip, s.hi[u].y ^ flip, s.hi[u].z ^ flip, s.hi[u].w ^ flip};
+        const Operand kb = to_operand(lo, hi);
         const float sabs = __builtin_fabsf(sc);
         f32x4 acc[TILES];
 #pragma unroll
-        for (int m = 0; m < TILES; ++m)
-          acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              qa[m], kb, f32x4{0, 0, 0, 0}, 0, 0, 0, 0, 0, 0);
+        for (int m = 0; m < TILES; ++m) {
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[0], kb.k[0], f32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+          for (int st = 1; st < 4; ++st)
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[st], kb.k[st], acc[m], 0, 0, 0);
+        }
 #pragma unroll
         for (int jl = 0; jl < JPG; ++jl) {
           float part = 0.0f;
@@ -215,12 +256,13 @@ using KernelFn = void (*)(Params);
 template <int TPJ, int JPG>
 constexpr KernelFn kfn() { return paged_logits_kernel<TPJ, JPG>; }
 
-// [TPJ-1][JPG-1]; TPJ = H/16 in 1..8, JPG = decode rows per wave = min(N, 8/TPJ).
+// [TPJ-1][JPG-1]; TPJ = H/16 in 1..8, JPG = decode rows per wave: min(N, 4/TPJ) for
+// H <= 64 (at most 4 row tiles, 64 f16 query VGPRs), 1 above (up to 8 row tiles).
 constexpr KernelFn kTable[8][4] = {
     {kfn<1, 1>(), kfn<1, 2>(), kfn<1, 3>(), kfn<1, 4>()},
-    {kfn<2, 1>(), kfn<2, 2>(), kfn<2, 3>(), kfn<2, 4>()},
-    {kfn<3, 1>(), kfn<3, 2>(), nullptr, nullptr},
-    {kfn<4, 1>(), kfn<4, 2>(), nullptr, nullptr},
+    {kfn<2, 1>(), kfn<2, 2>(), nullptr, nullptr},
+    {kfn<3, 1>(), nullptr, nullptr, nullptr},
+    {kfn<4, 1>(), nullptr, nullptr, nullptr},
     {kfn<5, 1>(), nullptr, nullptr, nullptr},
     {kfn<6, 1>(), nullptr, nullptr, nullptr},
     {kfn<7, 1>(), nullptr, nullptr, nullptr},
@@ -231,7 +273,8 @@ constexpr KernelFn kTable[8][4] = {
 
 hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   const int tpj = a.heads / 16;
-  const int jpg = a.next_n < 8 / tpj ? a.next_n : 8 / tpj;
+  const int per_wave = tpj <= 4 ? 4 / tpj : 1;
+  const int jpg = a.next_n < per_wave ? a.next_n : per_wave;
   const int groups = (a.next_n + jpg - 1) / jpg;
   const int slots = groups >= 4 ? 1 : 4 / groups;
   Params p;
