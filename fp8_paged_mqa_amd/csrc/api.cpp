@@ -11,6 +11,7 @@ namespace {
 constexpr int32_t kHeadDim = 128;
 constexpr int32_t kMaxTopk = 2048;
 constexpr int32_t kMaxModelLen = 1 << 30;
+constexpr int32_t kMaxBatch = 8192;  // the logits schedule keeps 3 ints per request in LDS
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -40,7 +41,7 @@ const char* mqa_status_string(int status) {
     case MQA_ERR_SHAPE: return "invalid shape or size";
     case MQA_ERR_UNSUPPORTED:
       return "unsupported: needs head_dim 128, block_size 1, heads a multiple of 16 up to 128, "
-             "next_n 1..4, max_model_len <= 2^30, k 1..2048, 16-byte aligned q and weights, "
+             "next_n 1..4, max_model_len <= 2^30, batch <= 8192 for the logits, k 1..2048, 16-byte aligned q and weights, "
              "4-byte aligned kv_cache, logits, idx and integer arrays";
     case MQA_ERR_WORKSPACE: return "workspace missing or too small";
     case MQA_ERR_HIP: return "HIP launch error";
@@ -54,6 +55,7 @@ int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* wei
                      hipStream_t stream) {
   const int st = check_shape(shape, max_model_len);
   if (st != MQA_OK) return st;
+  if (shape->batch > kMaxBatch) return MQA_ERR_UNSUPPORTED;
   if (shape->batch == 0) return MQA_OK;
   if (!q || !kv_cache || !weights || !context_lens || !block_tables || !out) return MQA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(weights, 16) || !aligned(kv_cache, 4) || !aligned(out, 4) ||
@@ -77,7 +79,7 @@ int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* wei
 
 size_t mqa_topk_workspace_bytes(const mqa_shape* shape, int32_t max_model_len, int32_t k) {
   if (check_shape(shape, max_model_len) != MQA_OK || k < 1 || k > kMaxTopk) return 0;
-  return 0;  // the single-pass-per-row kernel keeps all of its state in LDS
+  return mqa::topk_workspace_bytes((int64_t)shape->batch * shape->next_n, max_model_len);
 }
 
 int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model_len, int32_t k,
@@ -88,7 +90,8 @@ int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model
   if (k < 1) return MQA_ERR_SHAPE;
   if (k > kMaxTopk) return MQA_ERR_UNSUPPORTED;
   const size_t need = mqa_topk_workspace_bytes(shape, max_model_len, k);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MQA_ERR_WORKSPACE;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 8)))
+    return MQA_ERR_WORKSPACE;
   if (shape->batch == 0) return MQA_OK;
   if (!logits || !context_lens || !idx) return MQA_ERR_NULL;
   if (!aligned(logits, 4) || !aligned(context_lens, 4) || !aligned(idx, 4)) return MQA_ERR_UNSUPPORTED;
@@ -96,6 +99,7 @@ int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model
   a.logits = logits;
   a.ctx_lens = context_lens;
   a.idx = idx;
+  a.workspace = workspace;
   a.batch = shape->batch;
   a.next_n = shape->next_n;
   a.bt_stride = shape->block_table_stride;

@@ -24,8 +24,13 @@ struct TopkLaunch {
   const float* logits;
   const int32_t* ctx_lens;
   int32_t* idx;
+  void* workspace;  // topk_workspace_bytes(rows, max_model_len) bytes, 8-byte aligned
   int32_t batch, next_n, bt_stride, max_model_len, k;
 };
+
+// Device scratch the top-k launch needs for `rows` rows of length max_model_len
+// (0 when every row fits one workgroup).
+size_t topk_workspace_bytes(int64_t rows, int32_t max_model_len);
 
 // Enqueue the logits kernel on `stream`; returns the hipError_t of the launch.
 hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream);

@@ -14,11 +14,18 @@
 //     converted exactly to f16 (v_cvt_scalef32_pk_f16_fp8, scale 1) and contracted with
 //     v_mfma_f32_16x16x32_f16, four chained per 128-wide row: f16 products of e4m3
 //     values are exact and the fp32 accumulation is correctly rounded.
-//   * One wave owns a group of decode rows (at most 4 MFMA row tiles of 16 heads, so
-//     at most 64 query rows for H <= 64) and a contiguous token range. Its query rows stay
-//     in VGPRs, already in f16, in the A-operand layout, for the whole range. Decode rows
-//     beyond one wave's share go to sibling waves of the workgroup that walk the same
-//     tokens (their second read of a key row hits L2).
+//   * Schedule: one round of persistent workgroups (CUs x occupancy), so no workgroup
+//     waits for a slot. Each workgroup scans context_lens into LDS prefix sums; every
+//     wave then takes an equal contiguous share of all 64-token key stages of all
+//     requests (split at request boundaries into segments), and afterwards an equal
+//     share of the 1 KB chunks of -inf tail that lie past each request's last stage.
+//     The balance does not depend on how context lengths are distributed, and nothing
+//     is read from the device by the host.
+//   * One wave owns a group of decode rows (at most 4 MFMA row tiles of 16 heads, so at
+//     most 64 query rows for H <= 64). Its query rows stay in VGPRs, already in f16, in
+//     the A-operand layout, for a whole segment. Decode rows beyond one wave's share are
+//     other row groups: other waves walk the same stages for them (their second read of
+//     a key row hits L2).
 //   * Keys are gathered straight from HBM into the B-operand slots: lane (g, c),
 //     g = lane/16, c = lane%16, owns token c of a 16-token column tile and reads bytes
 //     [16g, 16g+16) and [64+16g, 64+16g+16) of that token's row, so each dwordx4 load
@@ -26,16 +33,19 @@
 //     and B use the same byte-to-k assignment, so the contraction covers all 128 k
 //     whatever order the hardware uses internally.
 //   * The block table is read 64 tokens at a time (one coalesced dword per lane) and
-//     redistributed with ds_bpermute; table reads run two 64-token stages ahead of use,
-//     key reads one stage ahead, so a wave keeps ~8 KB of gathers in flight.
+//     redistributed with ds_bpermute; table reads run two stages ahead of use, key reads
+//     one stage ahead. Every gather is issued unconditionally (a dead stage or a table
+//     entry outside the cache reads row 0 instead), so the loop is straight-line code
+//     and each compute waits only for its own stage's loads.
 //   * Epilogue in registers: the dequant scale's sign is folded into the fp8 key (flip
-//     the sign bit of every byte, exact), so relu(scale*s) = |scale| * relu(sign*s) and
-//     |scale| multiplies once per token after the head sum. Each lane sums w * relu over
-//     its 4 heads per row tile and the row tiles of a decode row, then two xor-shuffles
-//     finish the head sum across the 4 lane groups of a column.
+//     the sign bit of every byte, exact; skipped when no scale of the tile is negative),
+//     so relu(scale*s) = |scale| * relu(sign*s) and |scale| multiplies once per token
+//     after the head sum. Each lane sums w * relu over its 4 heads per row tile and the
+//     row tiles of a decode row; two xor-shuffles finish the sum across the 4 lane
+//     groups of a column.
 //   * Stores: after a 64-token stage each lane group keeps one 16-token column tile, so
-//     a row's 64 logits leave in one 256-byte store. Positions past the row's causal
-//     limit, and the whole tail up to L, are written with -inf in the same pass.
+//     a row's 64 logits leave in one 256-byte store; positions past a row's causal limit
+//     inside its last stage are written with -inf there.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -49,11 +59,14 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kD = 128;         // head_dim
-constexpr int kRow = kD + 4;    // cache row bytes: keys + fp32 scale
+constexpr int kD = 128;          // head_dim
+constexpr int kRow = kD + 4;     // cache row bytes: keys + fp32 scale
 constexpr int kWave = 64;
-constexpr int kStage = 64;      // tokens per pipeline stage = 4 MFMA column tiles
+constexpr int kWavesPerGroup = 4;  // waves per workgroup
+constexpr int kThreads = kWave * kWavesPerGroup;
+constexpr int kStage = 64;       // tokens per pipeline stage = 4 MFMA column tiles
 constexpr int kTilesPerStage = kStage / 16;
+constexpr int kTailChunk = 4 * kWave;  // floats per tail chunk: one float4 per lane
 
 struct Params {
   const uint8_t* q;
@@ -62,11 +75,10 @@ struct Params {
   const int32_t* ctx_lens;
   const int32_t* bt;
   float* out;
-  int64_t num_blocks;
+  uint32_t nblk;      // valid physical rows are [0, nblk) (num_blocks capped at 2^31 - 1)
   int32_t B, N, H, W, L;
-  int32_t groups;        // waves that share one token range, one per group of decode rows
-  int32_t slots;         // token ranges per workgroup
-  int32_t tok_per_wave;  // multiple of kStage
+  int32_t groups;     // row groups: waves that walk the same stages for different rows
+  int32_t vec_store;  // rows of `out` are 16-byte aligned (L % 4 == 0, aligned base)
 };
 
 __device__ __forceinline__ i32x4 load16(const uint8_t* p) {
@@ -107,147 +119,269 @@ struct Stage {
   i32x4 lo[kTilesPerStage];
   i32x4 hi[kTilesPerStage];
   float scale[kTilesPerStage];
+  int phys[kTilesPerStage];
 };
+
+// Exclusive scan of one int per thread over the workgroup (thread order).
+__device__ int block_exclusive_scan(int v, int* wave_tot) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_tot[w];
+  __syncthreads();
+  return before + incl - v;
+}
+
+// Largest index i in [0, n) with a[i] <= x (a nondecreasing, a[0] <= x).
+__device__ __forceinline__ int locate(const int* a, int n, int x) {
+  int lo = 0, hi = n;  // invariant: a[lo] <= x, answer < hi
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
 
 // Up to 4 row tiles fit two waves per SIMD (<= 256 VGPRs); the 5..8-tile variants
 // (H > 64) take the whole register file.
 template <int TPJ, int JPG>
-__global__ __launch_bounds__(256, (TPJ * JPG <= 4) ? 2 : 1) void paged_logits_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logits_kernel(Params p) {
   constexpr int TILES = TPJ * JPG;  // MFMA row tiles (16 heads each) held by one wave
   static_assert(TILES >= 1 && TILES <= 8, "query tile budget");
+
+  // LDS: clamped ctx per request, key-stage prefix, tail-chunk prefix, scan scratch.
+  extern __shared__ int lds[];
+  const int B = p.B;
+  int* ctx_s = lds;                     // [B]
+  int* stage_pref = lds + B;            // [B+1]
+  int* tail_pref = stage_pref + B + 1;  // [B+1]
+  int* scan_tmp = tail_pref + B + 1;    // [kWavesPerGroup]
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int g = lane >> 4;   // lane group: k-slice for operands, row quad for results
   const int c = lane & 15;   // column (token) / row (head) within a 16-wide tile
-  const int group = wave % p.groups;
-  const int slot = wave / p.groups;
+  const int L = p.L;
 
-  const int b = blockIdx.x % p.B;
-  const int range = blockIdx.x / p.B;
-  const int t0 = (range * p.slots + slot) * p.tok_per_wave;
-  if (t0 >= p.L) return;
-  const int t_end = min(t0 + p.tok_per_wave, p.L);
-
-  int ctx = p.ctx_lens[b];
-  ctx = max(0, min(ctx, min(p.W, p.L)));
-  const int t_need = min(t_end, ctx);  // positions whose key is read
-
-  const int j0 = group * JPG;           // first decode row of this wave
-  const int jn = min(JPG, p.N - j0);    // decode rows this wave owns
-  const int64_t out_row0 = (int64_t)(b * p.N + j0) * p.L;
-
-  // Query tiles (A operand) and the weights of the 4 heads each lane reduces per tile.
-  Operand qa[TILES];
-  f32x4 wv[TILES];
+  // ---- Schedule: per request, the number of 64-token key stages and of tail chunks.
   {
-    const uint8_t* qb = p.q + ((int64_t)b * p.N + j0) * p.H * kD;
-    const float* wb = p.w + ((int64_t)b * p.N + j0) * p.H;
+    const int per = (B + kThreads - 1) / kThreads;  // requests per thread, consecutive
+    const int r0 = threadIdx.x * per;
+    int stages = 0, chunks = 0;
+    for (int i = 0; i < per; ++i) {
+      const int b = r0 + i;
+      if (b < B) {
+        const int ctx = max(0, min(p.ctx_lens[b], min(p.W, L)));
+        const int ns = (ctx + kStage - 1) / kStage;
+        const int tail0 = ns * kStage;
+        const int nc = tail0 < L ? p.N * ((L - tail0 + kTailChunk - 1) / kTailChunk) : 0;
+        ctx_s[b] = ctx;
+        stage_pref[b] = ns;  // counts for now
+        tail_pref[b] = nc;
+        stages += ns;
+        chunks += nc;
+      }
+    }
+    const int s_excl = block_exclusive_scan(stages, scan_tmp);
+    const int c_excl = block_exclusive_scan(chunks, scan_tmp);
+    int s_run = s_excl, c_run = c_excl;
+    for (int i = 0; i < per; ++i) {
+      const int b = r0 + i;
+      if (b < B) {
+        const int ns = stage_pref[b], nc = tail_pref[b];
+        stage_pref[b] = s_run;
+        tail_pref[b] = c_run;
+        s_run += ns;
+        c_run += nc;
+      }
+    }
+    if (threadIdx.x == kThreads - 1) {
+      stage_pref[B] = s_run;
+      tail_pref[B] = c_run;
+    }
+    __syncthreads();
+  }
+
+  const int nwaves = gridDim.x * kWavesPerGroup;
+  const int gw = blockIdx.x * kWavesPerGroup + wave;
+
+  // ---- Key stages.
+  const int G = p.groups;
+  const int group = gw % G;
+  const int wi = gw / G;
+  const int nw = nwaves / G;
+  const int j0 = group * JPG;         // first decode row of this wave
+  const int jn = min(JPG, p.N - j0);  // decode rows this wave owns
+  if (wi < nw) {
+    const int S = stage_pref[B];
+    int lo = (int)((int64_t)wi * S / nw);
+    const int hi = (int)((int64_t)(wi + 1) * S / nw);
+    int b = lo < hi ? locate(stage_pref, B, lo) : 0;
+    const uint8_t* kv_g = p.kv + 16 * g;  // this lane's first key slice
+    const uint8_t* kv_s = p.kv + kD;      // scales
+    while (lo < hi) {
+      // Segment: stages [s0, s0 + nstage) of request b.
+      const int seg_hi = min(hi, stage_pref[b + 1]);
+      const int s0 = lo - stage_pref[b];
+      const int nstage = seg_hi - lo;
+      const int ctx = ctx_s[b];
+      const int t0 = s0 * kStage;
+      const int t_end = min((s0 + nstage) * kStage, L);
+      const int t_need = min(t_end, ctx);
+      float* const out0 = p.out + (int64_t)(b * p.N + j0) * L;
+
+      int nv[JPG];  // visible positions of each owned decode row
 #pragma unroll
-    for (int m = 0; m < TILES; ++m) {
-      const bool live = (m / TPJ) < jn;
-      const uint8_t* qr = qb + (m * 16 + c) * kD;
-      i32x4 a0 = live ? load16(qr + 16 * g) : i32x4{0, 0, 0, 0};
-      i32x4 a1 = live ? load16(qr + 64 + 16 * g) : i32x4{0, 0, 0, 0};
-      qa[m] = to_operand(a0, a1);
-      wv[m] = live ? *reinterpret_cast<const f32x4*>(wb + m * 16 + 4 * g) : f32x4{0, 0, 0, 0};
+      for (int jl = 0; jl < JPG; ++jl) nv[jl] = min(ctx - p.N + (j0 + jl) + 1, L);
+
+      const int32_t* btb = p.bt + (int64_t)b * p.W;
+      const int wmax = p.W - 1;
+      auto load_table = [&](int st) -> int {
+        return btb[st < nstage ? min(t0 + st * kStage + lane, wmax) : 0];
+      };
+      int tab0 = load_table(0);
+      int tab1 = load_table(1);
+
+      // Query tiles (A operand, f16) and the weights of the 4 heads each lane reduces.
+      Operand qa[TILES];
+      f32x4 wv[TILES];
+      {
+        const uint8_t* qb = p.q + ((int64_t)b * p.N + j0) * p.H * kD;
+        const float* wb = p.w + ((int64_t)b * p.N + j0) * p.H;
+#pragma unroll
+        for (int m = 0; m < TILES; ++m) {
+          const bool live = (m / TPJ) < jn;  // wave-uniform
+          const uint8_t* qr = qb + (m * 16 + c) * kD;
+          i32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+          wv[m] = f32x4{0, 0, 0, 0};
+          if (live) {
+            a0 = load16(qr + 16 * g);
+            a1 = load16(qr + 64 + 16 * g);
+            wv[m] = *reinterpret_cast<const f32x4*>(wb + m * 16 + 4 * g);
+          }
+          qa[m] = to_operand(a0, a1);
+        }
+      }
+
+      auto issue_keys = [&](int st, int tab, Stage& s) {
+        const bool live = st < nstage;  // wave-uniform
+        int ph[kTilesPerStage];
+#pragma unroll
+        for (int u = 0; u < kTilesPerStage; ++u) ph[u] = __shfl(tab, u * 16 + c);
+#pragma unroll
+        for (int u = 0; u < kTilesPerStage; ++u) {
+          const uint32_t row = (live && (uint32_t)ph[u] < p.nblk) ? (uint32_t)ph[u] : 0u;
+          const uint8_t* kp = kv_g + (uint64_t)row * kRow;
+          s.phys[u] = ph[u];
+          s.lo[u] = load16(kp);
+          s.hi[u] = load16(kp + 64);
+          s.scale[u] = *reinterpret_cast<const float*>(kv_s + (uint64_t)row * kRow);
+        }
+      };
+
+      auto compute_store = [&](int st, const Stage& s) {
+        const int tc = t0 + st * kStage;
+        float keep[JPG];
+#pragma unroll
+        for (int jl = 0; jl < JPG; ++jl) keep[jl] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < kTilesPerStage; ++u) {
+          const int t = tc + u * 16 + c;
+          const bool in_ctx = t < t_need;
+          const bool ok = in_ctx && (uint32_t)s.phys[u] < p.nblk;
+          // Past ctx the column is masked below; a bad table entry poisons it with NaN.
+          const float sc = ok ? s.scale[u] : (in_ctx ? __builtin_nanf("") : 0.0f);
+          i32x4 lo = s.lo[u], hi = s.hi[u];
+          if (__ballot(__float_as_int(sc) < 0) != 0) {  // wave-uniform: rare
+            const int flip = (__float_as_int(sc) < 0) ? (int)0x80808080 : 0;
+            lo ^= flip;
+            hi ^= flip;
+          }
+          const Operand kb = to_operand(lo, hi);
+          const float sabs = __builtin_fabsf(sc);
+          f32x4 acc[TILES];
+#pragma unroll
+          for (int m = 0; m < TILES; ++m) {
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[0], kb.k[0], f32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+            for (int k = 1; k < 4; ++k)
+              acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[k], kb.k[k], acc[m], 0, 0, 0);
+          }
+#pragma unroll
+          for (int jl = 0; jl < JPG; ++jl) {
+            float part = 0.0f;
+#pragma unroll
+            for (int mm = 0; mm < TPJ; ++mm) {
+              const int m = jl * TPJ + mm;
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                part = __builtin_fmaf(wv[m][v], __builtin_elementwise_maximum(acc[m][v], 0.0f), part);
+            }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            if (g == u) keep[jl] = part * sabs;
+          }
+        }
+        const int t = tc + lane;  // lane (g, c) stores token 16g + c of the stage
+        if (t < t_end) {
+#pragma unroll
+          for (int jl = 0; jl < JPG; ++jl)
+            if (jl < jn) out0[(int64_t)jl * L + t] = (t < nv[jl]) ? keep[jl] : -__builtin_inff();
+        }
+      };
+
+      // Software pipeline: table entries two stages ahead, keys one stage ahead.
+      Stage sa, sb;
+      issue_keys(0, tab0, sa);
+      for (int st = 0; st < nstage; st += 2) {
+        const int tab2 = load_table(st + 2);
+        issue_keys(st + 1, tab1, sb);
+        compute_store(st, sa);
+        if (st + 1 >= nstage) break;
+        tab1 = load_table(st + 3);
+        issue_keys(st + 2, tab2, sa);
+        compute_store(st + 1, sb);
+      }
+
+      lo = seg_hi;
+      ++b;
+      while (b < B && stage_pref[b + 1] <= lo) ++b;  // skip requests without stages
     }
   }
 
-  int nv[JPG];  // visible positions of each owned decode row
+  // ---- -inf tail: positions past each request's last key stage, every row.
+  {
+    const int C = tail_pref[B];
+    int ci = (int)((int64_t)gw * C / nwaves);
+    const int ce = (int)((int64_t)(gw + 1) * C / nwaves);
+    int b = ci < ce ? locate(tail_pref, B, ci) : 0;
+    const f32x4 ninf = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+    for (; ci < ce; ++ci) {
+      while (tail_pref[b + 1] <= ci) ++b;
+      const int tail0 = ((ctx_s[b] + kStage - 1) / kStage) * kStage;
+      const int per_row = (L - tail0 + kTailChunk - 1) / kTailChunk;
+      const int local = ci - tail_pref[b];
+      const int j = local / per_row;
+      const int start = tail0 + (local - j * per_row) * kTailChunk;
+      const int end = min(start + kTailChunk, L);
+      float* rp = p.out + (int64_t)(b * p.N + j) * L;
+      const int pos = start + 4 * lane;
+      if (p.vec_store && pos + 4 <= end) {
+        *reinterpret_cast<f32x4*>(rp + pos) = ninf;
+      } else {
 #pragma unroll
-  for (int jl = 0; jl < JPG; ++jl) nv[jl] = min(ctx - p.N + (j0 + jl) + 1, p.L);
-
-  const int32_t* btb = p.bt + (int64_t)b * p.W;
-
-  auto load_table = [&](int tc) -> int {
-    const int t = tc + lane;
-    return (t < t_need) ? btb[t] : -1;
-  };
-
-  auto issue_keys = [&](int tc, int tab, Stage& s) {
-#pragma unroll
-    for (int u = 0; u < kTilesPerStage; ++u) {
-      const int phys = __shfl(tab, u * 16 + c);
-      const int t = tc + u * 16 + c;
-      const bool in_ctx = t < t_need;
-      const bool ok = in_ctx && phys >= 0 && (int64_t)phys < p.num_blocks;
-      i32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-      float sc = in_ctx ? __builtin_nanf("") : 0.0f;  // bad table entry -> NaN logits
-      if (ok) {
-        const uint8_t* row = p.kv + (int64_t)phys * kRow;
-        lo = load16(row + 16 * g);
-        hi = load16(row + 64 + 16 * g);
-        sc = *reinterpret_cast<const float*>(row + kD);
-      }
-      s.lo[u] = lo;
-      s.hi[u] = hi;
-      s.scale[u] = sc;
-    }
-  };
-
-  auto compute_store = [&](int tc, const Stage& s) {
-    float keep[JPG];
-#pragma unroll
-    for (int jl = 0; jl < JPG; ++jl) keep[jl] = 0.0f;
-    if (tc < t_need) {
-#pragma unroll
-      for (int u = 0; u < kTilesPerStage; ++u) {
-        if (tc + u * 16 >= t_need) break;  // wave-uniform
-        const float sc = s.scale[u];
-        const int flip = (__float_as_int(sc) < 0) ? (int)0x80808080 : 0;
-        const i32x4 lo = {s.lo[u].x ^ flip, s.lo[u].y ^ flip, s.lo[u].z ^ flip, s.lo[u].w ^ flip};
-        const i32x4 hi = {s.hi[u].x ^ flip, s.hi[u].y ^ flip, s.hi[u].z ^ flip, s.hi[u].w ^ flip};
-        const Operand kb = to_operand(lo, hi);
-        const float sabs = __builtin_fabsf(sc);
-        f32x4 acc[TILES];
-#pragma unroll
-        for (int m = 0; m < TILES; ++m) {
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[0], kb.k[0], f32x4{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-          for (int st = 1; st < 4; ++st)
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[st], kb.k[st], acc[m], 0, 0, 0);
-        }
-#pragma unroll
-        for (int jl = 0; jl < JPG; ++jl) {
-          float part = 0.0f;
-#pragma unroll
-          for (int mm = 0; mm < TPJ; ++mm) {
-            const int m = jl * TPJ + mm;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              part = __builtin_fmaf(wv[m][v], __builtin_elementwise_maximum(acc[m][v], 0.0f), part);
-          }
-          part += __shfl_xor(part, 16);
-          part += __shfl_xor(part, 32);
-          if (g == u) keep[jl] = part * sabs;
-        }
+        for (int i = 0; i < 4; ++i)
+          if (pos + i < end) rp[pos + i] = -__builtin_inff();
       }
     }
-    const int t = tc + lane;  // lane (g, c) stores token 16g + c of the stage
-    if (t < t_end) {
-#pragma unroll
-      for (int jl = 0; jl < JPG; ++jl) {
-        if (jl < jn) p.out[out_row0 + (int64_t)jl * p.L + t] = (t < nv[jl]) ? keep[jl] : -__builtin_inff();
-      }
-    }
-  };
-
-  // Software pipeline: table two stages ahead, keys one stage ahead.
-  int tc = t0;
-  int tab_next = load_table(tc + kStage);
-  Stage s0, s1;
-  issue_keys(tc, load_table(tc), s0);
-  while (tc < t_end) {
-    int tab_after = load_table(tc + 2 * kStage);
-    issue_keys(tc + kStage, tab_next, s1);
-    compute_store(tc, s0);
-    tc += kStage;
-    if (tc >= t_end) break;
-    tab_next = load_table(tc + 2 * kStage);
-    issue_keys(tc + kStage, tab_after, s0);
-    compute_store(tc, s1);
-    tc += kStage;
   }
 }
 
@@ -269,14 +403,27 @@ constexpr KernelFn kTable[8][4] = {
     {kfn<8, 1>(), nullptr, nullptr, nullptr},
 };
 
+// Compute units of the current device, read once per device.
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+  }
+  return n;
+}
+
+size_t logits_lds_bytes(int32_t batch) { return (size_t)(3 * (int64_t)batch + 2 + kWavesPerGroup) * 4; }
+
 }  // namespace
 
 hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   const int tpj = a.heads / 16;
   const int per_wave = tpj <= 4 ? 4 / tpj : 1;
   const int jpg = a.next_n < per_wave ? a.next_n : per_wave;
-  const int groups = (a.next_n + jpg - 1) / jpg;
-  const int slots = groups >= 4 ? 1 : 4 / groups;
   Params p;
   p.q = a.q;
   p.kv = a.kv;
@@ -284,21 +431,22 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   p.ctx_lens = a.ctx_lens;
   p.bt = a.bt;
   p.out = a.out;
-  p.num_blocks = a.num_blocks;
+  p.nblk = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
   p.B = a.batch;
   p.N = a.next_n;
   p.H = a.heads;
   p.W = a.bt_stride;
   p.L = a.max_model_len;
-  p.groups = groups;
-  p.slots = slots;
-  p.tok_per_wave = 2 * kStage;
-  const int64_t per_wg = (int64_t)slots * p.tok_per_wave;
-  const int64_t ranges = (a.max_model_len + per_wg - 1) / per_wg;
-  const int64_t blocks = ranges * a.batch;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  p.groups = (a.next_n + jpg - 1) / jpg;
+  p.vec_store = (a.max_model_len % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
   KernelFn fn = kTable[tpj - 1][jpg - 1];
-  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(groups * slots * kWave), 0, stream, p);
+  const size_t lds = logits_lds_bytes(a.batch);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, lds) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int blocks = compute_units() * per_cu;
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 

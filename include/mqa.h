@@ -49,7 +49,8 @@ enum {
 
 /*
  * Problem shape (host struct).
- *   batch               B, number of requests (>= 0; 0 enqueues nothing)
+ *   batch               B, number of requests (>= 0; 0 enqueues nothing; at most 8192
+ *                       for mqa_paged_logits)
  *   next_n              N, decode rows per request (speculative depth + 1), 1..4
  *   heads               H, index query heads, a multiple of 16 in [16, 128]
  *   head_dim            D, must be 128
@@ -117,8 +118,10 @@ int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* wei
  *   k               1 .. 2048
  *   idx             int32  [B*N, k]
  *   workspace       device scratch of at least mqa_topk_workspace_bytes(shape,
- *                   max_model_len, k) bytes; contents on entry do not matter, the
- *                   call initialises what it uses, in stream order
+ *                   max_model_len, k) bytes, 8-byte aligned (may be NULL when that
+ *                   size is 0, i.e. max_model_len <= 8192); contents on entry do not
+ *                   matter, the call initialises what it uses, in stream order. Calls
+ *                   that overlap in time must not share a workspace.
  * Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED,
  * MQA_ERR_WORKSPACE or MQA_ERR_HIP.
  */

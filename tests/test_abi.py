@@ -105,6 +105,11 @@ def test_misaligned_pointers():
     assert call_logits(good_shape(), ptrs=(FAKE, FAKE, q_off) + (FAKE,) * 3) == mqa.MQA_ERR_UNSUPPORTED
 
 
+def test_logits_batch_limit():
+    assert call_logits(good_shape(batch=8193)) == mqa.MQA_ERR_UNSUPPORTED
+    assert call_topk(good_shape(batch=8193)) != mqa.MQA_ERR_UNSUPPORTED
+
+
 def test_topk_k_range():
     assert call_topk(good_shape(), k=0) == mqa.MQA_ERR_SHAPE
     assert call_topk(good_shape(), k=2049) == mqa.MQA_ERR_UNSUPPORTED
