@@ -9,28 +9,28 @@
 //   e = key(logit) << 32 | (0xFFFFFFFF - position)
 // where key() is the order-preserving map of an fp32 onto uint32 (-0 folded onto +0).
 // Larger e means "selected earlier", and e is unique per position, so the top k of a
-// row is exactly the k largest e: a radix select over e needs no tie rule of its own.
-// Digits of e, most significant first: 11, 11, 10 bits of the key, then 11, 11, 10
-// bits of the position part (only reached when the k-th key is tied).
+// row is exactly the k largest e; no separate tie rule is needed.
 //
-// Rows with nv <= k select every visible position without reading the logits.
-//
-// Rows with k < nv <= kChunk (8192): one workgroup of 1024 threads owns the row. Each
-// thread loads its 8 logits in one batch and keeps their keys in registers; an LDS
-// histogram of the top 11 key bits and a block scan from the top find the bin of the
-// k-th element; one pass over the registers emits every element of a higher bin
-// (wave ballot + mbcnt compaction, one LDS atomic per wave) and copies the threshold
-// bin into an LDS candidate list, which the remaining digits refine the same way.
-//
-// Longer rows are split into 8192-element chunks, one workgroup each:
-//   hist   each chunk adds its LDS histogram into the row's global histogram;
-//   split  each chunk finds the threshold bin from the global histogram, emits its
-//          elements above it straight to the output (global atomic slot counter per
-//          row) and appends its threshold-bin elements to the row's candidate list;
-//   finish one workgroup per row refines the candidates in LDS. If the threshold bin
-//          holds more than kCap elements (extreme ties, e.g. a constant row) it
-//          refines over the whole row from global memory instead: slower, same result.
-// A fill kernel clears the histograms and counters first, in stream order.
+// Row classes (nv known only on the device):
+//   trivial  nv <= k: every visible position, no logits read.
+//   short    k < nv <= 8192: one workgroup of 1024 threads owns the row, 8 logits per
+//            thread in registers. A block min/max reduction sets 2048 first-level bins
+//            linear in the value (monotone, so bins are ordered like the logits; rows
+//            holding a non-finite value use the top 12 key bits instead). An LDS
+//            histogram and a block scan from the top find the bin holding the k-th
+//            element; everything above it is emitted at offsets from one block scan,
+//            and the threshold bin's elements go to an LDS candidate list. A small list
+//            is finished by counting, for each candidate, the candidates above it; a
+//            large one by further 11-bit radix digits of e.
+//   long     nv > 8192: 8192-element chunks. A schedule kernel lists the long rows and
+//            their chunks and clears their histograms; persistent kernels then add each
+//            chunk's 12-bit key histogram into the row's global histogram, emit each
+//            chunk's elements above the threshold bin (one global atomic per workgroup
+//            reserves the output slots) and collect its threshold-bin elements, and
+//            finish each row's candidates in LDS. If the threshold bin holds more than
+//            kCap elements (extreme ties, e.g. a constant row) the finish refines over
+//            the whole row from global memory: slower, same result.
+// When max_model_len <= 8192 no row can be long: one launch, one workgroup per row.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -40,25 +40,31 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kPer = 8;                     // logits per thread per chunk
-constexpr int kChunk = kThreads * kPer;     // 8192
-constexpr int kBins = 2048;
-constexpr int kCap = 8192;                  // LDS candidate slots (64 KB)
+constexpr int kPer = 8;                   // logits per thread per chunk
+constexpr int kChunk = kThreads * kPer;   // 8192
+constexpr int kLinBins = 2048;            // first level of a short row (linear bins)
+constexpr int kKeyBits = 12;              // first level of a long row (top key bits)
+constexpr int kKeyBins = 1 << kKeyBits;   // 4096
+constexpr int kCap = 8192;                // LDS candidate slots (64 KB)
+constexpr int kRankMax = 256;             // candidate lists up to this size are ranked
+
+enum { kMetaLong = 0, kMetaChunks = 1, kMetaShort = 2, kMetaTrivial = 3 };
 
 struct Params {
   const float* logits;
   const int32_t* ctx_lens;
   int32_t* idx;
-  uint32_t* hist;      // [rows][kBins]
-  uint32_t* counters;  // [rows][2]: emitted, candidates
-  uint64_t* cand;      // [rows][kCap]
-  int32_t N, W, L, k, nchunk;
+  // Workspace (long-row mode only; null otherwise).
+  uint32_t* meta;         // [8]: long rows, long chunks, short rows, trivial rows
+  uint32_t* long_rows;    // [rows] row id of each long-row slot
+  uint32_t* short_rows;   // [rows]
+  uint32_t* triv_rows;    // [rows]
+  uint32_t* chunk_items;  // [rows * nchunk_max][2]: long-row slot, chunk
+  uint32_t* counters;     // [rows][2] per slot: emitted, candidates
+  uint32_t* hist;         // [rows][kKeyBins] per slot
+  uint64_t* cand;         // [rows][kCap] per slot
+  int32_t rows, N, W, L, k;
 };
-
-__device__ __forceinline__ int digit_shift(int level) {
-  return level == 0 ? 53 : level == 1 ? 42 : level == 2 ? 32 : level == 3 ? 21 : level == 4 ? 10 : 0;
-}
-__device__ __forceinline__ int digit_width(int level) { return (level == 2 || level == 5) ? 10 : 11; }
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -72,33 +78,26 @@ __device__ __forceinline__ uint64_t compose(uint32_t key, int t) {
 
 __device__ __forceinline__ int position(uint64_t e) { return (int)(0xFFFFFFFFu - (uint32_t)e); }
 
-// Row geometry shared by all kernels.
-struct Row {
-  int r, nv, k;
-  __device__ Row(const Params& p, int row) : r(row), k(p.k) {
-    const int b = row / p.N;
-    const int j = row - b * p.N;
-    int ctx = p.ctx_lens[b];
-    ctx = max(0, min(ctx, min(p.W, p.L)));
-    nv = max(0, min(ctx - p.N + j + 1, p.L));
-  }
-};
+__device__ __forceinline__ int visible(const Params& p, int row) {
+  const int b = row / p.N;
+  const int j = row - b * p.N;
+  const int ctx = max(0, min(p.ctx_lens[b], min(p.W, p.L)));
+  return max(0, min(ctx - p.N + j + 1, p.L));
+}
 
 struct Core {
-  uint32_t hist[kBins];
-  uint32_t wave_sum[kWaves];
-  uint32_t n_out;
-  uint32_t n_cand;
-  uint32_t bin;
-  uint32_t above;
+  uint32_t hist[kKeyBins];
+  uint32_t red[2 * kWaves];
+  uint32_t n_out, n_cand, bin, above, base_a, base_b, item;
+  float vmin, vmax;
+  uint32_t nonfinite;
 };
 
 struct Full : Core {
   uint64_t cand[kCap];
 };
 
-// Wave-aggregated append: lanes with `pred` get consecutive slots from *counter (LDS or
-// global). Must be called by all 64 lanes of the wave. Returns the slot (or -1).
+// Wave-aggregated append to an LDS counter. Must be called by all 64 lanes of a wave.
 __device__ __forceinline__ int wave_append(bool pred, uint32_t* counter) {
   const uint64_t mask = __ballot(pred);
   if (mask == 0) return -1;
@@ -113,7 +112,7 @@ __device__ __forceinline__ int wave_append(bool pred, uint32_t* counter) {
 }
 
 // Exclusive prefix sum over the 1024 threads in thread order.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Core& sh) {
+__device__ uint32_t block_exclusive_scan(uint32_t v, Core& sh) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   uint32_t incl = v;
@@ -122,70 +121,102 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Core& sh) {
     const uint32_t o = __shfl_up(incl, d);
     if (lane >= d) incl += o;
   }
-  if (lane == 63) sh.wave_sum[wave] = incl;
+  if (lane == 63) sh.red[wave] = incl;
   __syncthreads();
   uint32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += sh.wave_sum[w];
+  for (int w = 0; w < wave; ++w) before += sh.red[w];
   __syncthreads();
   return before + incl - v;
 }
 
-// Finds the bin B (scanning from the top) with above(B) < rem <= above(B) + hist[B].
-// Leaves B in sh.bin and above(B) in sh.above. All threads must call it.
-__device__ void find_bin(Core& sh, uint32_t rem) {
+// Finds the bin B (scanning from the top of nbins) with above(B) < rem <= above(B) +
+// hist[B]; leaves B in sh.bin and above(B) in sh.above. All threads must call it.
+__device__ void find_bin(Core& sh, int nbins, uint32_t rem) {
+  const int per = nbins / kThreads;  // 2 or 4
+  const int top = nbins - 1 - per * (int)threadIdx.x;
+  uint32_t cnt[4] = {0, 0, 0, 0}, sum = 0;
+  for (int i = 0; i < per; ++i) {
+    cnt[i] = sh.hist[top - i];
+    sum += cnt[i];
+  }
   if (threadIdx.x == 0) {
     sh.bin = 0;
     sh.above = 0;
   }
-  const int hi = kBins - 1 - 2 * (int)threadIdx.x;
-  const int lo = hi - 1;
-  const uint32_t ch = sh.hist[hi], cl = sh.hist[lo];
-  const uint32_t excl = block_exclusive_scan(ch + cl, sh);
-  if (excl < rem && rem <= excl + ch) {
-    sh.bin = (uint32_t)hi;
-    sh.above = excl;
-  } else if (excl + ch < rem && rem <= excl + ch + cl) {
-    sh.bin = (uint32_t)lo;
-    sh.above = excl + ch;
+  uint32_t run = block_exclusive_scan(sum, sh);
+  for (int i = 0; i < per; ++i) {
+    if (run < rem && rem <= run + cnt[i]) {
+      sh.bin = (uint32_t)(top - i);
+      sh.above = run;
+    }
+    run += cnt[i];
   }
   __syncthreads();
 }
 
-__device__ __forceinline__ void clear_hist(Core& sh) {
-  for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist[i] = 0;
+__device__ __forceinline__ void clear_hist(Core& sh, int nbins) {
+  for (int i = threadIdx.x; i < nbins; i += kThreads) sh.hist[i] = 0;
   __syncthreads();
 }
 
-// Keys of the chunk starting at `base`: element i of thread tid is base + i*1024 + tid.
-// All loads are issued before any is used (addresses clamped into the row).
-__device__ __forceinline__ void load_chunk(const float* row, int base, int nv, uint32_t (&key)[kPer]) {
-  float v[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) v[i] = row[min(base + i * kThreads + (int)threadIdx.x, nv - 1)];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) key[i] = order_key(v[i]);
+// Reserves na (nb) consecutive slots of *ca (*cb) for each thread with one atomic per
+// counter for the whole block; returns this thread's first slots.
+__device__ void block_reserve2(uint32_t na, uint32_t nb, uint32_t* ca, uint32_t* cb, Core& sh,
+                               uint32_t& oa, uint32_t& ob) {
+  const uint32_t packed = (na << 16) | nb;  // na, nb <= kPer: block totals < 2^16
+  const uint32_t excl = block_exclusive_scan(packed, sh);
+  if (threadIdx.x == kThreads - 1) {
+    const uint32_t tot = excl + packed;
+    sh.base_a = atomicAdd(ca, tot >> 16);
+    sh.base_b = atomicAdd(cb, tot & 0xFFFFu);
+  }
+  __syncthreads();
+  oa = sh.base_a + (excl >> 16);
+  ob = sh.base_b + (excl & 0xFFFFu);
+  __syncthreads();
 }
 
-// Refinement over the LDS candidate list (FromRow = false) or the whole row filtered by
-// the level-0 prefix (FromRow = true). `rem` elements are still to be taken from those
-// matching `prefix` under `pmask`; emitted positions go to out[sh.n_out++].
+// Loads element i*1024 + tid of the chunk at `base` for i < kPer (addresses clamped
+// into the row; all loads issued before any is used).
+__device__ __forceinline__ void load_chunk(const float* row, int base, int nv, float (&v)[kPer]) {
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) v[i] = row[min(base + i * kThreads + (int)threadIdx.x, nv - 1)];
+}
+
+// Selects the `rem` largest of the n candidates in sh.cand by counting, for each, the
+// candidates above it. n <= kRankMax.
+__device__ void rank_select(Full& sh, int n, uint32_t rem, int32_t* out, int k) {
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const uint64_t e = sh.cand[i];
+    uint32_t rank = 0;
+    for (int j = 0; j < n; ++j) rank += sh.cand[j] > e ? 1u : 0u;
+    if (rank < rem) {
+      const uint32_t slot = atomicAdd(&sh.n_out, 1u);
+      if (slot < (uint32_t)k) out[slot] = position(e);
+    }
+  }
+  __syncthreads();
+}
+
+// Radix refinement over the candidate list (FromRow = false) or the whole visible row
+// (FromRow = true), for elements matching `prefix` under `pmask`; bits [0, top) of e are
+// still undecided. Emits through sh.n_out.
 template <bool FromRow>
-__device__ void refine(Full& sh, const float* row, int n, uint64_t prefix, uint64_t pmask,
+__device__ void refine(Full& sh, const float* row, int n, uint64_t prefix, uint64_t pmask, int top,
                        uint32_t rem, int32_t* out, int k) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   auto fetch = [&](int i) -> uint64_t { return FromRow ? compose(order_key(row[i]), i) : sh.cand[i]; };
-
-  for (int level = 1; level < 6; ++level) {
-    const int shift = digit_shift(level);
-    const uint64_t dmask = (1ull << digit_width(level)) - 1;
-    clear_hist(sh);
+  while (top > 0) {
+    const int shift = top > 11 ? top - 11 : 0;
+    const uint64_t dmask = (1ull << (top - shift)) - 1;
+    clear_hist(sh, kLinBins);
     for (int i = threadIdx.x; i < n; i += kThreads) {
       const uint64_t e = fetch(i);
       if ((e & pmask) == prefix) atomicAdd(&sh.hist[(e >> shift) & dmask], 1u);
     }
     __syncthreads();
-    find_bin(sh, rem);
+    find_bin(sh, kLinBins, rem);
     const uint64_t bin = sh.bin;
     const uint32_t above = sh.above;
     const uint32_t cnt = sh.hist[bin];
@@ -199,6 +230,7 @@ __device__ void refine(Full& sh, const float* row, int n, uint64_t prefix, uint6
     rem -= above;
     prefix |= bin << shift;
     pmask |= dmask << shift;
+    top = shift;
     __syncthreads();
     if (cnt == rem) {  // the whole threshold bin is selected
       for (int base = wave * 64; base < n; base += kThreads) {
@@ -207,190 +239,391 @@ __device__ void refine(Full& sh, const float* row, int n, uint64_t prefix, uint6
         const int slot = wave_append(i < n && (e & pmask) == prefix, &sh.n_out);
         if (slot >= 0 && slot < k) out[slot] = position(e);
       }
+      __syncthreads();
       return;
     }
   }
 }
 
-// Whole select of a row with k < nv <= kChunk by one workgroup.
-__device__ void select_short_row(const Params& p, const Row& row_info, Full& sh) {
-  const int nv = row_info.nv, k = row_info.k;
-  const float* row = p.logits + (int64_t)row_info.r * p.L;
-  int32_t* out = p.idx + (int64_t)row_info.r * k;
+// Finishes the candidate list sh.cand[0, n) (all matching prefix/pmask, bits [0, top)
+// undecided): `rem` of them are selected.
+__device__ void finish_candidates(Full& sh, int n, uint64_t prefix, uint64_t pmask, int top, uint32_t rem,
+                                  int32_t* out, int k) {
+  if (n <= kRankMax)
+    rank_select(sh, n, rem, out, k);
+  else
+    refine<false>(sh, nullptr, n, prefix, pmask, top, rem, out, k);
+}
 
-  uint32_t key[kPer];
-  load_chunk(row, 0, nv, key);
-  clear_hist(sh);
+// Rows with nv <= k.
+__device__ void select_trivial_row(const Params& p, int r, int nv) {
+  int32_t* out = p.idx + (int64_t)r * p.k;
+  for (int i = threadIdx.x; i < p.k; i += kThreads) out[i] = i < nv ? i : -1;
+}
+
+// Rows with k < nv <= kChunk: the whole select by one workgroup.
+__device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
+  const int k = p.k;
+  const float* row = p.logits + (int64_t)r * p.L;
+  int32_t* out = p.idx + (int64_t)r * k;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+
+  float v[kPer];
+  load_chunk(row, 0, nv, v);
+  // Block min/max over the visible values; any non-finite value switches to key bins.
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  uint32_t bad = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (i * kThreads + (int)threadIdx.x < nv) {
+      if (__builtin_isfinite(v[i])) {
+        lo = fminf(lo, v[i]);
+        hi = fmaxf(hi, v[i]);
+      } else {
+        bad = 1;
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, d));
+    hi = fmaxf(hi, __shfl_xor(hi, d));
+  }
+  const uint64_t bad_mask = __ballot(bad != 0);
+  if (lane == 0) {
+    sh.red[wave] = __float_as_uint(lo);
+    sh.red[kWaves + wave] = __float_as_uint(hi);
+  }
   if (threadIdx.x == 0) {
+    sh.nonfinite = 0;
     sh.n_out = 0;
     sh.n_cand = 0;
   }
+  __syncthreads();
+  if (lane == 0 && bad_mask) sh.nonfinite = 1;  // benign race: every writer stores 1
+  lo = __builtin_inff();
+  hi = -__builtin_inff();
+  for (int w = 0; w < kWaves; ++w) {
+    lo = fminf(lo, __uint_as_float(sh.red[w]));
+    hi = fmaxf(hi, __uint_as_float(sh.red[kWaves + w]));
+  }
+  // Binning: linear in the value when the visible values are finite and spread; by the
+  // top key bits when some value is not finite (or the spread is not representable);
+  // a single bin when all values are equal (then the refinement starts at bit 64).
+  const bool nonfinite = sh.nonfinite != 0;
+  __syncthreads();
+  const float spread = hi - lo;
+  const float scale = kLinBins / spread;
+  const bool linear = !nonfinite && hi > lo && __builtin_isfinite(spread) && __builtin_isfinite(scale) && scale > 0.0f;
+  const bool keyed = !linear && (nonfinite || hi > lo);
+  const int nbins = keyed ? kKeyBins : kLinBins;
+  uint32_t key[kPer], bin[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    key[i] = order_key(v[i]);
+    bin[i] = linear ? (uint32_t)min(kLinBins - 1, (int)((v[i] - lo) * scale))
+                    : (keyed ? key[i] >> (32 - kKeyBits) : 0u);
+  }
+  clear_hist(sh, nbins);
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if (i * kThreads + (int)threadIdx.x < nv) atomicAdd(&sh.hist[key[i] >> 21], 1u);
+    if (i * kThreads + (int)threadIdx.x < nv) atomicAdd(&sh.hist[bin[i]], 1u);
   __syncthreads();
-  find_bin(sh, (uint32_t)k);
+  find_bin(sh, nbins, (uint32_t)k);
   const uint32_t bin0 = sh.bin;
   const uint32_t rem = (uint32_t)k - sh.above;
   const uint32_t cnt0 = sh.hist[bin0];
   const bool whole = cnt0 == rem;
+  // Emit the elements above the threshold bin, collect the bin's elements.
+  uint32_t na = 0, nb = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const bool in = i * kThreads + (int)threadIdx.x < nv;
+    na += (in && (bin[i] > bin0 || (whole && bin[i] == bin0))) ? 1u : 0u;
+    nb += (in && !whole && bin[i] == bin0) ? 1u : 0u;
+  }
+  uint32_t oa, ob;
+  block_reserve2(na, nb, &sh.n_out, &sh.n_cand, sh, oa, ob);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int t = i * kThreads + (int)threadIdx.x;
     const bool in = t < nv;
-    const uint32_t d = key[i] >> 21;
-    const int slot = wave_append(in && (d > bin0 || (whole && d == bin0)), &sh.n_out);
-    if (slot >= 0 && slot < k) out[slot] = t;
-    const int cslot = wave_append(in && !whole && d == bin0, &sh.n_cand);
-    if (cslot >= 0 && cslot < kCap) sh.cand[cslot] = compose(key[i], t);
+    if (in && (bin[i] > bin0 || (whole && bin[i] == bin0))) {
+      if (oa < (uint32_t)k) out[oa] = t;
+      ++oa;
+    } else if (in && !whole && bin[i] == bin0) {
+      if (ob < (uint32_t)kCap) sh.cand[ob] = compose(key[i], t);
+      ++ob;
+    }
   }
   __syncthreads();
-  if (!whole) refine<false>(sh, row, (int)cnt0, (uint64_t)bin0 << 53, 0x7FFull << 53, rem, out, k);
+  if (!whole) {
+    // Key bins fix the top 12 bits of e; linear or single bins fix none.
+    const uint64_t prefix = keyed ? (uint64_t)bin0 << (64 - kKeyBits) : 0ull;
+    const uint64_t pmask = keyed ? (uint64_t)(kKeyBins - 1) << (64 - kKeyBits) : 0ull;
+    finish_candidates(sh, (int)cnt0, prefix, pmask, keyed ? 64 - kKeyBits : 64, rem, out, k);
+  }
 }
 
-// Rows with nv <= k, and rows that fit one chunk, are finished here by chunk 0's workgroup.
-// Longer rows: this chunk's histogram is added into the row's global histogram.
-__global__ __launch_bounds__(kThreads) void topk_hist_kernel(Params p) {
+// Pass 1. Implicit mode (no workspace): workgroup r handles row r. Scheduled mode:
+// persistent workgroups walk long-row chunks (histograms), then short rows, then
+// trivial rows.
+__global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
   __shared__ Full sh;
-  const int r = blockIdx.x / p.nchunk;
-  const int ch = blockIdx.x - r * p.nchunk;
-  const Row ri(p, r);
-  const int nv = ri.nv, k = ri.k;
-  if (nv <= kChunk || nv <= k) {
-    if (ch != 0) return;
-    int32_t* out = p.idx + (int64_t)r * k;
-    const int m = min(k, nv);
-    for (int i = m + threadIdx.x; i < k; i += kThreads) out[i] = -1;
-    if (nv <= k) {
-      for (int t = threadIdx.x; t < nv; t += kThreads) out[t] = t;
-      return;
-    }
-    select_short_row(p, ri, sh);
+  if (p.meta == nullptr) {
+    const int r = blockIdx.x;
+    const int nv = visible(p, r);
+    if (nv <= p.k) select_trivial_row(p, r, nv);
+    else select_short_row(p, r, nv, sh);
     return;
   }
-  const int base = ch * kChunk;
-  if (base >= nv) return;
-  const float* row = p.logits + (int64_t)r * p.L;
-  uint32_t key[kPer];
-  load_chunk(row, base, nv, key);
-  clear_hist(sh);
+  const int nc = (int)p.meta[kMetaChunks];
+  const int ns = (int)p.meta[kMetaShort];
+  const int nt = (int)p.meta[kMetaTrivial];
+  for (int item = blockIdx.x; item < nc + ns + nt; item += gridDim.x) {
+    if (item < nc) {
+      const int slot = (int)p.chunk_items[2 * item];
+      const int ch = (int)p.chunk_items[2 * item + 1];
+      const int r = (int)p.long_rows[slot];
+      const int nv = visible(p, r);
+      const int base = ch * kChunk;
+      float v[kPer];
+      load_chunk(p.logits + (int64_t)r * p.L, base, nv, v);
+      clear_hist(sh, kKeyBins);
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (base + i * kThreads + (int)threadIdx.x < nv) atomicAdd(&sh.hist[key[i] >> 21], 1u);
-  __syncthreads();
-  uint32_t* gh = p.hist + (int64_t)r * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) {
-    const uint32_t v = sh.hist[i];
-    if (v) atomicAdd(&gh[i], v);
+      for (int i = 0; i < kPer; ++i)
+        if (base + i * kThreads + (int)threadIdx.x < nv) atomicAdd(&sh.hist[order_key(v[i]) >> (32 - kKeyBits)], 1u);
+      __syncthreads();
+      uint32_t* gh = p.hist + (int64_t)slot * kKeyBins;
+      for (int i = threadIdx.x; i < kKeyBins; i += kThreads) {
+        const uint32_t c = sh.hist[i];
+        if (c) atomicAdd(&gh[i], c);
+      }
+      __syncthreads();
+    } else if (item < nc + ns) {
+      const int r = (int)p.short_rows[item - nc];
+      select_short_row(p, r, visible(p, r), sh);
+      __syncthreads();
+    } else {
+      const int r = (int)p.triv_rows[item - nc - ns];
+      select_trivial_row(p, r, visible(p, r));
+    }
   }
 }
 
-// Long rows: threshold bin from the global histogram, emit the elements above it,
-// collect the elements in it.
+// Schedule for long-row mode (one workgroup): classifies every row, lists the rows of
+// each class and the long rows' chunks (offsets from block scans), and clears the long
+// rows' histograms and counters.
+__global__ __launch_bounds__(kThreads) void topk_schedule_kernel(Params p) {
+  __shared__ Core sh;
+  uint32_t off_l = 0, off_s = 0, off_t = 0, off_c = 0;
+  for (int base = 0; base < p.rows; base += kThreads) {
+    const int r = base + (int)threadIdx.x;
+    const bool in = r < p.rows;
+    const int nv = in ? visible(p, r) : 0;
+    const uint32_t is_long = in && nv > p.k && nv > kChunk;
+    const uint32_t is_short = in && nv > p.k && nv <= kChunk;
+    const uint32_t is_triv = in && nv <= p.k;
+    const uint32_t nch = is_long ? (uint32_t)((nv + kChunk - 1) / kChunk) : 0u;
+    const uint32_t el = block_exclusive_scan(is_long | (is_short << 16), sh);  // < 2^16 each
+    const uint32_t et = block_exclusive_scan(is_triv, sh);
+    const uint32_t ec = block_exclusive_scan(nch, sh);
+    if (is_long) {
+      const uint32_t slot = off_l + (el & 0xFFFFu);
+      p.long_rows[slot] = (uint32_t)r;
+      p.counters[2 * slot] = 0u;
+      p.counters[2 * slot + 1] = 0u;
+      const uint32_t first = off_c + ec;
+      for (uint32_t c = 0; c < nch; ++c) {
+        p.chunk_items[2 * (first + c)] = slot;
+        p.chunk_items[2 * (first + c) + 1] = c;
+      }
+    }
+    if (is_short) p.short_rows[off_s + (el >> 16)] = (uint32_t)r;
+    if (is_triv) p.triv_rows[off_t + et] = (uint32_t)r;
+    if (threadIdx.x == kThreads - 1) {
+      sh.base_a = el + (is_long | (is_short << 16));
+      sh.base_b = et + is_triv;
+      sh.item = ec + nch;
+    }
+    __syncthreads();
+    off_l += sh.base_a & 0xFFFFu;
+    off_s += sh.base_a >> 16;
+    off_t += sh.base_b;
+    off_c += sh.item;
+    __syncthreads();
+  }
+  uint2* gh = reinterpret_cast<uint2*>(p.hist);
+  const int64_t words2 = (int64_t)off_l * (kKeyBins / 2);
+  for (int64_t i = threadIdx.x; i < words2; i += kThreads) gh[i] = make_uint2(0u, 0u);
+  if (threadIdx.x == 0) {
+    p.meta[kMetaLong] = off_l;
+    p.meta[kMetaChunks] = off_c;
+    p.meta[kMetaShort] = off_s;
+    p.meta[kMetaTrivial] = off_t;
+  }
+}
+
+// Pass 2 (long rows): threshold bin from the row's histogram; emit the chunk's elements
+// above it, collect those in it.
 __global__ __launch_bounds__(kThreads) void topk_split_kernel(Params p) {
   __shared__ Core sh;
-  const int r = blockIdx.x / p.nchunk;
-  const int ch = blockIdx.x - r * p.nchunk;
-  const Row ri(p, r);
-  const int nv = ri.nv, k = ri.k;
-  if (nv <= kChunk || nv <= k) return;
-  const int base = ch * kChunk;
-  if (base >= nv) return;
-  const float* row = p.logits + (int64_t)r * p.L;
-  uint32_t key[kPer];
-  load_chunk(row, base, nv, key);
-  const uint32_t* gh = p.hist + (int64_t)r * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist[i] = gh[i];
-  __syncthreads();
-  find_bin(sh, (uint32_t)k);
-  const uint32_t bin0 = sh.bin;
-  const uint32_t rem = (uint32_t)k - sh.above;
-  const bool whole = sh.hist[bin0] == rem;
-  int32_t* out = p.idx + (int64_t)r * k;
-  uint32_t* cnt = p.counters + 2 * (int64_t)r;
-  uint64_t* cand = p.cand + (int64_t)r * kCap;
+  const int nc = (int)p.meta[kMetaChunks];
+  for (int item = blockIdx.x; item < nc; item += gridDim.x) {
+    const int slot = (int)p.chunk_items[2 * item];
+    const int ch = (int)p.chunk_items[2 * item + 1];
+    const int r = (int)p.long_rows[slot];
+    const int nv = visible(p, r);
+    const int k = p.k;
+    const int base = ch * kChunk;
+    float v[kPer];
+    load_chunk(p.logits + (int64_t)r * p.L, base, nv, v);
+    const uint32_t* gh = p.hist + (int64_t)slot * kKeyBins;
+    for (int i = threadIdx.x; i < kKeyBins; i += kThreads) sh.hist[i] = gh[i];
+    __syncthreads();
+    find_bin(sh, kKeyBins, (uint32_t)k);
+    const uint32_t bin0 = sh.bin;
+    const bool whole = sh.hist[bin0] == (uint32_t)k - sh.above;
+    uint32_t key[kPer];
+    uint32_t na = 0, nb = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int t = base + i * kThreads + (int)threadIdx.x;
-    const bool in = t < nv;
-    const uint32_t d = key[i] >> 21;
-    const int slot = wave_append(in && (d > bin0 || (whole && d == bin0)), &cnt[0]);
-    if (slot >= 0 && slot < k) out[slot] = t;
-    const int cslot = wave_append(in && !whole && d == bin0, &cnt[1]);
-    if (cslot >= 0 && cslot < kCap) cand[cslot] = compose(key[i], t);
+    for (int i = 0; i < kPer; ++i) {
+      key[i] = order_key(v[i]);
+      const uint32_t d = key[i] >> (32 - kKeyBits);
+      const bool in = base + i * kThreads + (int)threadIdx.x < nv;
+      na += (in && (d > bin0 || (whole && d == bin0))) ? 1u : 0u;
+      nb += (in && !whole && d == bin0) ? 1u : 0u;
+    }
+    uint32_t oa, ob;
+    block_reserve2(na, nb, &p.counters[2 * slot], &p.counters[2 * slot + 1], sh, oa, ob);
+    int32_t* out = p.idx + (int64_t)r * k;
+    uint64_t* cand = p.cand + (int64_t)slot * kCap;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int t = base + i * kThreads + (int)threadIdx.x;
+      const uint32_t d = key[i] >> (32 - kKeyBits);
+      const bool in = t < nv;
+      if (in && (d > bin0 || (whole && d == bin0))) {
+        if (oa < (uint32_t)k) out[oa] = t;
+        ++oa;
+      } else if (in && !whole && d == bin0) {
+        if (ob < (uint32_t)kCap) cand[ob] = compose(key[i], t);
+        ++ob;
+      }
+    }
+    __syncthreads();
   }
 }
 
-// Long rows: refine the threshold-bin candidates.
+// Pass 3 (long rows): refine each row's candidates.
 __global__ __launch_bounds__(kThreads) void topk_finish_kernel(Params p) {
   __shared__ Full sh;
-  const int r = blockIdx.x;
-  const Row ri(p, r);
-  const int nv = ri.nv, k = ri.k;
-  if (nv <= kChunk || nv <= k) return;
-  const uint32_t* gh = p.hist + (int64_t)r * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist[i] = gh[i];
-  __syncthreads();
-  find_bin(sh, (uint32_t)k);
-  const uint32_t bin0 = sh.bin;
-  const uint32_t above = sh.above;
-  const uint32_t rem = (uint32_t)k - above;
-  const uint32_t cnt0 = sh.hist[bin0];
-  if (cnt0 == rem) return;  // the split pass took the whole bin
-  const float* row = p.logits + (int64_t)r * p.L;
-  int32_t* out = p.idx + (int64_t)r * k;
-  if (threadIdx.x == 0) sh.n_out = above;  // the split pass emitted exactly `above`
-  if (cnt0 <= (uint32_t)kCap) {
-    const uint64_t* cand = p.cand + (int64_t)r * kCap;
-    for (int i = threadIdx.x; i < (int)cnt0; i += kThreads) sh.cand[i] = cand[i];
+  const int nl = (int)p.meta[kMetaLong];
+  for (int slot = blockIdx.x; slot < nl; slot += gridDim.x) {
+    const int r = (int)p.long_rows[slot];
+    const int nv = visible(p, r);
+    const int k = p.k;
+    const uint32_t* gh = p.hist + (int64_t)slot * kKeyBins;
+    for (int i = threadIdx.x; i < kKeyBins; i += kThreads) sh.hist[i] = gh[i];
     __syncthreads();
-    refine<false>(sh, row, (int)cnt0, (uint64_t)bin0 << 53, 0x7FFull << 53, rem, out, k);
-  } else {
+    find_bin(sh, kKeyBins, (uint32_t)k);
+    const uint32_t bin0 = sh.bin;
+    const uint32_t above = sh.above;
+    const uint32_t rem = (uint32_t)k - above;
+    const uint32_t cnt0 = sh.hist[bin0];
     __syncthreads();
-    refine<true>(sh, row, nv, (uint64_t)bin0 << 53, 0x7FFull << 53, rem, out, k);
+    if (cnt0 == rem) continue;  // the split pass took the whole bin (uniform)
+    const float* row = p.logits + (int64_t)r * p.L;
+    int32_t* out = p.idx + (int64_t)r * k;
+    if (threadIdx.x == 0) sh.n_out = above;  // the split pass emitted exactly `above`
+    const uint64_t prefix = (uint64_t)bin0 << (64 - kKeyBits);
+    const uint64_t pmask = (uint64_t)(kKeyBins - 1) << (64 - kKeyBits);
+    if (cnt0 <= (uint32_t)kCap) {
+      const uint64_t* cand = p.cand + (int64_t)slot * kCap;
+      for (int i = threadIdx.x; i < (int)cnt0; i += kThreads) sh.cand[i] = cand[i];
+      __syncthreads();
+      finish_candidates(sh, (int)cnt0, prefix, pmask, 64 - kKeyBits, rem, out, k);
+    } else {
+      __syncthreads();
+      refine<true>(sh, row, nv, prefix, pmask, 64 - kKeyBits, rem, out, k);
+    }
+    __syncthreads();
   }
 }
 
-__global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
+// Workspace layout (long-row mode): meta[8] | long_rows | short_rows | triv_rows |
+// chunk_items | counters | hist | cand, each region 8-byte aligned.
+struct Layout {
+  size_t meta, long_rows, short_rows, triv_rows, chunk_items, counters, hist, cand, total;
+};
+
+Layout layout(int64_t rows, int32_t L) {
+  auto up8 = [](size_t x) { return (x + 7) & ~(size_t)7; };
+  const int64_t nchunk = (L + kChunk - 1) / kChunk;
+  Layout l;
+  l.meta = 0;
+  l.long_rows = 32;
+  l.short_rows = up8(l.long_rows + 4 * rows);
+  l.triv_rows = up8(l.short_rows + 4 * rows);
+  l.chunk_items = up8(l.triv_rows + 4 * rows);
+  l.counters = up8(l.chunk_items + 8 * rows * nchunk);
+  l.hist = up8(l.counters + 8 * rows);
+  l.cand = up8(l.hist + (size_t)4 * kKeyBins * rows);
+  l.total = l.cand + (size_t)8 * kCap * rows;
+  return l;
+}
+
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+  }
+  return n;
 }
 
 }  // namespace
 
 size_t topk_workspace_bytes(int64_t rows, int32_t max_model_len) {
   if (max_model_len <= kChunk) return 0;
-  return (size_t)rows * ((size_t)kBins * 4 + 2 * 4 + (size_t)kCap * 8);
+  return layout(rows, max_model_len).total;
 }
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.batch * a.next_n;
-  Params p;
+  if (rows > 0x7fffffff) return hipErrorInvalidConfiguration;
+  Params p = {};
   p.logits = a.logits;
   p.ctx_lens = a.ctx_lens;
   p.idx = a.idx;
+  p.rows = (int32_t)rows;
   p.N = a.next_n;
   p.W = a.bt_stride;
   p.L = a.max_model_len;
   p.k = a.k;
-  p.nchunk = (a.max_model_len + kChunk - 1) / kChunk;
-  // Workspace: histograms, then counters, then candidates (8-byte aligned).
+  if (a.max_model_len <= kChunk) {  // every row fits one workgroup
+    hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+  }
+  const Layout l = layout(rows, a.max_model_len);
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
-  p.hist = reinterpret_cast<uint32_t*>(ws);
-  p.counters = reinterpret_cast<uint32_t*>(ws + rows * kBins * 4);
-  p.cand = reinterpret_cast<uint64_t*>(ws + rows * (kBins * 4 + 8));
-  if (rows * p.nchunk > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (p.nchunk > 1) {
-    const int64_t words = rows * (kBins + 2);
-    const int64_t blocks = (words + 255) / 256;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0,
-                       stream, p.hist, words);
-  }
-  hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)(rows * p.nchunk)), dim3(kThreads), 0, stream, p);
-  if (p.nchunk > 1) {
-    hipLaunchKernelGGL(topk_split_kernel, dim3((unsigned)(rows * p.nchunk)), dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
-  }
+  p.meta = reinterpret_cast<uint32_t*>(ws + l.meta);
+  p.long_rows = reinterpret_cast<uint32_t*>(ws + l.long_rows);
+  p.short_rows = reinterpret_cast<uint32_t*>(ws + l.short_rows);
+  p.triv_rows = reinterpret_cast<uint32_t*>(ws + l.triv_rows);
+  p.chunk_items = reinterpret_cast<uint32_t*>(ws + l.chunk_items);
+  p.counters = reinterpret_cast<uint32_t*>(ws + l.counters);
+  p.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
+  p.cand = reinterpret_cast<uint64_t*>(ws + l.cand);
+  const unsigned persistent = (unsigned)compute_units();
+  hipLaunchKernelGGL(topk_schedule_kernel, dim3(1), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(persistent), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(topk_split_kernel, dim3(persistent), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(persistent), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
