@@ -2,18 +2,25 @@
 
     python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
 
-One step = mqa_paged_logits + mqa_topk over one batch of the named synthetic
-workload (inputs already resident in HBM). The timed region is exactly K steps
-bracketed by torch.cuda.synchronize(); value = indexed KV tokens (sum of context
-lengths) per second. Steps rotate over enough copies of the inputs that every step
-reads buffers evicted from the 256 MB Infinity Cache by the steps in between.
+One step = mqa_paged_logits + mqa_topk over one batch of the named synthetic workload,
+inputs already resident in HBM. Steps are captured into a HIP graph and replayed (the
+indexer runs once per layer per decode step, so serving stacks replay it from graphs;
+eager launches from Python cost more host time than the GPU work). Consecutive steps
+rotate over `--copies` copies of the inputs and outputs, so every step reads buffers
+that the steps in between have evicted from the 256 MB Infinity Cache.
 
-Prints one JSON line with, besides the headline value:
-  roofline      the logits kernel (the dominant one) against HBM: algorithmic bytes
-                per launch / its mean launch time, the latter from HIP events around
-                each launch in a separate instrumented pass of K steps;
-  cpu_baseline  the CPU oracle (float64, numpy) on the same workload, timed on this
-                host's cores; a reported baseline, not a target.
+Timed region: exactly K steps (graph replays), bracketed by torch.cuda.synchronize().
+value = indexed KV tokens (sum of context lengths) per second of that region.
+
+The JSON line also carries:
+  roofline      the logits kernel (the dominant one) against HBM: algorithmic bytes per
+                launch / its mean launch time, from HIP events on the launch stream around
+                graphs of back-to-back logits launches (same rotation);
+  traffic       measured HBM bytes per logits launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+                scaled by the copy calibration) from the committed profile summary, when
+                that summary was taken on the current kernel source;
+  cpu_baseline  the CPU oracle (float64 numpy) on the same workload on this host's cores;
+                a reported baseline, not a target.
 """
 from __future__ import annotations
 
@@ -32,12 +39,11 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "indexed KV tokens/s (logits+top-2048) and % HBM peak, H=64 D=128 fp8"
 ROW_BYTES = 132
 LOGITS_SRC = os.path.join(ROOT, "fp8_paged_mqa_amd", "csrc", "logits.hip")
-TOPK_SRC = os.path.join(ROOT, "fp8_paged_mqa_amd", "csrc", "topk.hip")
 
 
 def algorithmic_bytes(w):
-    """Bytes the logits and top-k launches must move at minimum (each input read
-    once, each output written once)."""
+    """Bytes each launch must move at minimum: every input read once, every output
+    written once."""
     sum_ctx = w.sum_ctx
     rows = w.rows
     nv = w.visible().astype(np.int64)
@@ -55,8 +61,8 @@ def source_digest(path):
 
 
 def traffic_from_profile(kernel, workload_tag, digest):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if one exists for
-    this kernel source; None otherwise."""
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary taken on this kernel
+    source; None otherwise."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_pmc.md")
     if not os.path.exists(path):
         return None
@@ -82,20 +88,22 @@ def cpu_baseline(w, min_seconds=10.0):
         oracle.topk(o, w.context_lens, w.next_n, w.k, w.max_model_len)
         runs += 1
         el = time.perf_counter() - t0
-        if el >= min_seconds or runs >= 20:
+        if el >= min_seconds or runs >= 1000:
             break
     return {"value": w.sum_ctx * runs / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"the whole workload (logits + top-{w.k}), {runs} run(s), {el:.1f} s, float64 numpy"}
+            "sample": f"the whole workload (logits + top-{w.k}, float64 numpy), {runs} run(s) in {el:.1f} s"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=256,
+                    help="size of the plain device copy run once for counter calibration (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -111,8 +119,10 @@ def main():
     dev = "cuda"
     shape = mqa.make_shape(w.batch, w.next_n, w.heads, w.num_blocks, w.block_tables.shape[1])
     L, k = w.max_model_len, w.k
+    C = max(1, args.copies)
+    ws_bytes = max(1, mqa.mqa_topk_workspace_bytes(shape, L, k))
     copies = []
-    for _ in range(max(1, args.copies)):
+    for _ in range(C):
         copies.append(dict(
             q=torch.from_numpy(w.q).to(dev), kv=torch.from_numpy(w.kv_cache).to(dev),
             w=torch.from_numpy(w.weights).to(dev),
@@ -120,7 +130,7 @@ def main():
             bt=torch.from_numpy(w.block_tables.astype(np.int32)).to(dev),
             out=torch.empty((w.rows, L), dtype=torch.float32, device=dev),
             idx=torch.empty((w.rows, k), dtype=torch.int32, device=dev),
-            ws=torch.empty(max(1, mqa.mqa_topk_workspace_bytes(shape, L, k)), dtype=torch.uint8, device=dev)))
+            ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
 
     def logits(c):
         mqa.mqa_paged_logits(c["q"], c["kv"], c["w"], c["ctx"], c["bt"], L, c["out"], shape)
@@ -128,41 +138,77 @@ def main():
     def topk(c):
         mqa.mqa_topk(c["out"], c["ctx"], L, k, c["idx"], shape, c["ws"])
 
-    for i in range(args.warmup):
-        c = copies[i % len(copies)]
+    def step(c):
         logits(c)
         topk(c)
+
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(copies[i % C])
+        return g
+
+    # Eager warmup (also loads the code objects), then the graphs.
+    for i in range(4):
+        step(copies[i % C])
+    torch.cuda.synchronize()
+    g_steps = capture(step, C)                 # C steps, one per input copy
+    rem = args.steps % C
+    g_rem = capture(step, rem) if rem else None
+    for _ in range(max(1, args.warmup // C)):
+        g_steps.replay()
     torch.cuda.synchronize()
 
     # Timed region: exactly K steps.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        c = copies[i % len(copies)]
-        logits(c)
-        topk(c)
+    for _ in range(args.steps // C):
+        g_steps.replay()
+    if g_rem is not None:
+        g_rem.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # Instrumented pass: HIP events around each launch on the launch stream.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Per-kernel mean launch time: HIP events on the launch stream around graphs of
+    # back-to-back launches of one kernel.
+    def per_launch_us(fn, reps=8):
+        g = capture(fn, C)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * C)
+
+    t_logits = per_launch_us(logits)
+    t_topk = per_launch_us(topk)
+
+    # Host-launched steps (no graph), for reference.
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        c = copies[i % len(copies)]
-        ev[i][0].record()
-        logits(c)
-        ev[i][1].record()
-        topk(c)
-        ev[i][2].record()
+    t1 = time.perf_counter()
+    n_eager = min(args.steps, 50)
+    for i in range(n_eager):
+        step(copies[i % C])
     torch.cuda.synchronize()
-    t_logits = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
-    t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    eager_ms = (time.perf_counter() - t1) * 1e3 / n_eager
+
+    if args.calibrate_copy_mib > 0:  # a plain copy of known size, for counter calibration
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     bytes_logits, bytes_topk = algorithmic_bytes(w)
-    achieved = bytes_logits / t_logits / 1e9
-    tag = f"config{args.config}"
-    traffic = traffic_from_profile("logits", tag, source_digest(LOGITS_SRC))
+    achieved = bytes_logits / (t_logits * 1e-6) / 1e9
+    traffic = traffic_from_profile("logits", f"config{args.config}", source_digest(LOGITS_SRC))
     value = w.sum_ctx / (ms_per_step * 1e-3)
     step_gbps = (bytes_logits + bytes_topk) / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -176,21 +222,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3fn-mfma/f32",
+        "dtype": "fp8e4m3fn->f16 mfma, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "next_n": w.next_n, "heads": w.heads,
                    "head_dim": 128, "block_size": 1, "max_model_len": L, "k": k,
-                   "sum_ctx": w.sum_ctx, "pool_rows": w.num_blocks, "input_copies": len(copies)},
+                   "sum_ctx": w.sum_ctx, "pool_rows": w.num_blocks, "input_copies": C,
+                   "timing": "HIP graph replay of the step"},
         "hbm_frac_step": step_gbps / HBM_PEAK_GBPS,
-        "kernels_us": {"logits": t_logits * 1e6, "topk": t_topk * 1e6},
+        "kernels_us": {"logits": t_logits, "topk": t_topk},
+        "eager_ms_per_step": eager_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "kernel": "paged_logits_kernel",
-                     "algorithmic_bytes": bytes_logits,
-                     "traffic": traffic},
+                     "algorithmic_bytes": bytes_logits, "traffic": traffic},
     }
     if not args.no_cpu_baseline:
-        wc = workloads.make_config(args.config, poison_unused=False)
-        result["cpu_baseline"] = cpu_baseline(wc)
+        result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)
 
 

@@ -154,3 +154,42 @@ def test_out_of_range_device_values_are_contained():
         mask[b, t] = False
     g2, o2 = np.where(mask, g, 0.0), np.where(mask, o, 0.0)
     check_logits(g2.astype(np.float32), o2, "contained")
+
+
+def test_graph_replay_matches_eager():
+    """The calls allocate nothing and never synchronise, so a step captures into a HIP
+    graph. Replays, with eager work and host syncs in between, must equal the eager
+    result every time (long rows: the four-kernel top-k path)."""
+    import torch
+    from fp8_paged_mqa_amd import mqa
+    from gpu_helpers import device_inputs, shape_of
+    case = wl.make_case(batch=4, next_n=2, heads=64, ctx=[20000, 9000, 100, 3000],
+                        max_model_len=20000, seed=58)
+    d = device_inputs(case)
+    shape = shape_of(case)
+    L, k = case.max_model_len, case.k
+    out = torch.empty((case.rows, L), dtype=torch.float32, device="cuda")
+    idx = torch.empty((case.rows, k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, mqa.mqa_topk_workspace_bytes(shape, L, k)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        mqa.mqa_paged_logits(d["q"], d["kv"], d["w"], d["ctx"], d["bt"], L, out, shape)
+        mqa.mqa_topk(out, d["ctx"], L, k, idx, shape, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_logits = out.clone()
+    ref_idx = torch.sort(idx, dim=1).values
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref_logits.view(torch.int32)), rep
+        assert torch.equal(torch.sort(idx, dim=1).values, ref_idx), rep
+        step()  # eager work between replays
+        torch.cuda.synchronize()
