@@ -33,10 +33,12 @@
 //     and B use the same byte-to-k assignment, so the contraction covers all 128 k
 //     whatever order the hardware uses internally.
 //   * The block table is read 64 tokens at a time (one coalesced dword per lane) and
-//     redistributed with ds_bpermute; table reads run two stages ahead of use, key reads
-//     one stage ahead. Every gather is issued unconditionally (a dead stage or a table
-//     entry outside the cache reads row 0 instead), so the loop is straight-line code
-//     and each compute waits only for its own stage's loads.
+//     redistributed with ds_bpermute. A wave keeps the keys of two 64-token stages in
+//     flight (~17 KB), the table entries two stages ahead of their use, and issues its
+//     first two stages before converting its query rows. Every gather is issued
+//     unconditionally (a dead stage or a table entry outside the cache reads row 0
+//     instead), so the loop is straight-line code and each compute waits only for its
+//     own stage's loads.
 //   * Epilogue in registers: the dequant scale's sign is folded into the fp8 key (flip
 //     the sign bit of every byte, exact; skipped when no scale of the tile is negative),
 //     so relu(scale*s) = |scale| * relu(sign*s) and |scale| multiplies once per token
@@ -250,8 +252,9 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
       int tab0 = load_table(0);
       int tab1 = load_table(1);
 
-      // Query tiles (A operand, f16) and the weights of the 4 heads each lane reduces.
-      Operand qa[TILES];
+      // Query rows of this segment: raw bytes now, f16 A operands once the first key
+      // gathers are on their way (the conversion then overlaps their latency).
+      i32x4 qraw[TILES][2];
       f32x4 wv[TILES];
       {
         const uint8_t* qb = p.q + ((int64_t)b * p.N + j0) * p.H * kD;
@@ -260,16 +263,17 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         for (int m = 0; m < TILES; ++m) {
           const bool live = (m / TPJ) < jn;  // wave-uniform
           const uint8_t* qr = qb + (m * 16 + c) * kD;
-          i32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+          qraw[m][0] = i32x4{0, 0, 0, 0};
+          qraw[m][1] = i32x4{0, 0, 0, 0};
           wv[m] = f32x4{0, 0, 0, 0};
           if (live) {
-            a0 = load16(qr + 16 * g);
-            a1 = load16(qr + 64 + 16 * g);
+            qraw[m][0] = load16(qr + 16 * g);
+            qraw[m][1] = load16(qr + 64 + 16 * g);
             wv[m] = *reinterpret_cast<const f32x4*>(wb + m * 16 + 4 * g);
           }
-          qa[m] = to_operand(a0, a1);
         }
       }
+      Operand qa[TILES];
 
       auto issue_keys = [&](int st, int tab, Stage& s) {
         const bool live = st < nstage;  // wave-uniform
@@ -338,17 +342,25 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         }
       };
 
-      // Software pipeline: table entries two stages ahead, keys one stage ahead.
+      // Software pipeline: keys of two stages in flight, table entries two stages ahead
+      // of their use; the compute of stage s waits only for stage s's loads, and its
+      // registers are refilled with stage s+2 right after.
       Stage sa, sb;
       issue_keys(0, tab0, sa);
+      issue_keys(1, tab1, sb);
+      tab0 = load_table(2);
+      tab1 = load_table(3);
+#pragma unroll
+      for (int m = 0; m < TILES; ++m) qa[m] = to_operand(qraw[m][0], qraw[m][1]);
       for (int st = 0; st < nstage; st += 2) {
-        const int tab2 = load_table(st + 2);
-        issue_keys(st + 1, tab1, sb);
         compute_store(st, sa);
         if (st + 1 >= nstage) break;
-        tab1 = load_table(st + 3);
-        issue_keys(st + 2, tab2, sa);
+        issue_keys(st + 2, tab0, sa);
+        tab0 = load_table(st + 4);
         compute_store(st + 1, sb);
+        if (st + 2 >= nstage) break;
+        issue_keys(st + 3, tab1, sb);
+        tab1 = load_table(st + 5);
       }
 
       lo = seg_hi;

@@ -85,12 +85,15 @@ __device__ __forceinline__ int visible(const Params& p, int row) {
   return max(0, min(ctx - p.N + j + 1, p.L));
 }
 
+// Per-wave scratch slots, one region per use so that consecutive block operations need
+// no barrier between them for the scratch itself.
+enum { kRedLo = 0, kRedHi = kWaves, kRedBad = 2 * kWaves, kRedBin = 3 * kWaves, kRedEmit = 4 * kWaves,
+       kRedSize = 5 * kWaves };
+
 struct Core {
   uint32_t hist[kKeyBins];
-  uint32_t red[2 * kWaves];
-  uint32_t n_out, n_cand, bin, above, base_a, base_b, item;
-  float vmin, vmax;
-  uint32_t nonfinite;
+  uint32_t red[kRedSize];
+  uint32_t n_out, n_cand, bin, above, base_a, base_b;
 };
 
 struct Full : Core {
@@ -111,21 +114,52 @@ __device__ __forceinline__ int wave_append(bool pred, uint32_t* counter) {
   return pred ? (int)(base + below) : -1;
 }
 
-// Exclusive prefix sum over the 1024 threads in thread order.
-__device__ uint32_t block_exclusive_scan(uint32_t v, Core& sh) {
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then row broadcasts).
+__device__ __forceinline__ uint32_t wave_scan_add(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Running min / max over the lanes (lane 63 ends with the wave's value).
+template <bool Max, int Ctrl, int Rows>
+__device__ __forceinline__ float minmax_step(float v) {
+  const int id = __float_as_int(Max ? -__builtin_inff() : __builtin_inff());
+  const float o = __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), Ctrl, Rows, 0xf, false));
+  return Max ? fmaxf(v, o) : fminf(v, o);
+}
+
+template <bool Max>
+__device__ __forceinline__ float wave_scan_minmax(float v) {
+  v = minmax_step<Max, 0x111, 0xf>(v);  // row_shr:1
+  v = minmax_step<Max, 0x112, 0xf>(v);  // row_shr:2
+  v = minmax_step<Max, 0x114, 0xf>(v);  // row_shr:4
+  v = minmax_step<Max, 0x118, 0xf>(v);  // row_shr:8
+  v = minmax_step<Max, 0x142, 0xa>(v);  // row_bcast:15
+  v = minmax_step<Max, 0x143, 0xc>(v);  // row_bcast:31
+  return v;
+}
+
+// Exclusive prefix sum over the 1024 threads in thread order, through the kWaves scratch
+// slots at `slot`. Also returns the block total. One barrier.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Core& sh, int slot, uint32_t& total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t incl = v;
+  const uint32_t incl = wave_scan_add(v);
+  if (lane == 63) sh.red[slot + wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t t = sh.red[slot + w];
+    before += w < wave ? t : 0u;
+    all += t;
   }
-  if (lane == 63) sh.red[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += sh.red[w];
-  __syncthreads();
+  total = all;
   return before + incl - v;
 }
 
@@ -143,7 +177,8 @@ __device__ void find_bin(Core& sh, int nbins, uint32_t rem) {
     sh.bin = 0;
     sh.above = 0;
   }
-  uint32_t run = block_exclusive_scan(sum, sh);
+  uint32_t total;
+  uint32_t run = block_exclusive_scan(sum, sh, kRedBin, total);
   for (int i = 0; i < per; ++i) {
     if (run < rem && rem <= run + cnt[i]) {
       sh.bin = (uint32_t)(top - i);
@@ -164,9 +199,9 @@ __device__ __forceinline__ void clear_hist(Core& sh, int nbins) {
 __device__ void block_reserve2(uint32_t na, uint32_t nb, uint32_t* ca, uint32_t* cb, Core& sh,
                                uint32_t& oa, uint32_t& ob) {
   const uint32_t packed = (na << 16) | nb;  // na, nb <= kPer: block totals < 2^16
-  const uint32_t excl = block_exclusive_scan(packed, sh);
-  if (threadIdx.x == kThreads - 1) {
-    const uint32_t tot = excl + packed;
+  uint32_t tot;
+  const uint32_t excl = block_exclusive_scan(packed, sh, kRedEmit, tot);
+  if (threadIdx.x == 0) {
     sh.base_a = atomicAdd(ca, tot >> 16);
     sh.base_b = atomicAdd(cb, tot & 0xFFFFu);
   }
@@ -271,9 +306,10 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
 
   float v[kPer];
   load_chunk(row, 0, nv, v);
-  // Block min/max over the visible values; any non-finite value switches to key bins.
+  for (int i = threadIdx.x; i < kKeyBins; i += kThreads) sh.hist[i] = 0;
+  // Min / max of the visible values; any non-finite value switches to key bins.
   float lo = __builtin_inff(), hi = -__builtin_inff();
-  uint32_t bad = 0;
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if (i * kThreads + (int)threadIdx.x < nv) {
@@ -281,38 +317,29 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
         lo = fminf(lo, v[i]);
         hi = fmaxf(hi, v[i]);
       } else {
-        bad = 1;
+        bad = true;
       }
     }
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    lo = fminf(lo, __shfl_xor(lo, d));
-    hi = fmaxf(hi, __shfl_xor(hi, d));
-  }
-  const uint64_t bad_mask = __ballot(bad != 0);
-  if (lane == 0) {
-    sh.red[wave] = __float_as_uint(lo);
-    sh.red[kWaves + wave] = __float_as_uint(hi);
-  }
-  if (threadIdx.x == 0) {
-    sh.nonfinite = 0;
-    sh.n_out = 0;
-    sh.n_cand = 0;
+  lo = wave_scan_minmax<false>(lo);
+  hi = wave_scan_minmax<true>(hi);
+  const bool wave_bad = __ballot(bad) != 0;
+  if (lane == 63) {
+    sh.red[kRedLo + wave] = __float_as_uint(lo);
+    sh.red[kRedHi + wave] = __float_as_uint(hi);
+    sh.red[kRedBad + wave] = wave_bad ? 1u : 0u;
   }
   __syncthreads();
-  if (lane == 0 && bad_mask) sh.nonfinite = 1;  // benign race: every writer stores 1
-  lo = __builtin_inff();
-  hi = -__builtin_inff();
+  bool nonfinite = false;
+#pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    lo = fminf(lo, __uint_as_float(sh.red[w]));
-    hi = fmaxf(hi, __uint_as_float(sh.red[kWaves + w]));
+    lo = fminf(lo, __uint_as_float(sh.red[kRedLo + w]));
+    hi = fmaxf(hi, __uint_as_float(sh.red[kRedHi + w]));
+    nonfinite |= sh.red[kRedBad + w] != 0;
   }
   // Binning: linear in the value when the visible values are finite and spread; by the
   // top key bits when some value is not finite (or the spread is not representable);
   // a single bin when all values are equal (then the refinement starts at bit 64).
-  const bool nonfinite = sh.nonfinite != 0;
-  __syncthreads();
   const float spread = hi - lo;
   const float scale = kLinBins / spread;
   const bool linear = !nonfinite && hi > lo && __builtin_isfinite(spread) && __builtin_isfinite(scale) && scale > 0.0f;
@@ -324,18 +351,16 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
     key[i] = order_key(v[i]);
     bin[i] = linear ? (uint32_t)min(kLinBins - 1, (int)((v[i] - lo) * scale))
                     : (keyed ? key[i] >> (32 - kKeyBits) : 0u);
-  }
-  clear_hist(sh, nbins);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
     if (i * kThreads + (int)threadIdx.x < nv) atomicAdd(&sh.hist[bin[i]], 1u);
+  }
   __syncthreads();
   find_bin(sh, nbins, (uint32_t)k);
   const uint32_t bin0 = sh.bin;
   const uint32_t rem = (uint32_t)k - sh.above;
   const uint32_t cnt0 = sh.hist[bin0];
   const bool whole = cnt0 == rem;
-  // Emit the elements above the threshold bin, collect the bin's elements.
+  // Emit the elements above the threshold bin (slots from 0), collect the bin's
+  // elements into the LDS candidate list (slots from 0).
   uint32_t na = 0, nb = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -343,8 +368,9 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
     na += (in && (bin[i] > bin0 || (whole && bin[i] == bin0))) ? 1u : 0u;
     nb += (in && !whole && bin[i] == bin0) ? 1u : 0u;
   }
-  uint32_t oa, ob;
-  block_reserve2(na, nb, &sh.n_out, &sh.n_cand, sh, oa, ob);
+  uint32_t total;
+  const uint32_t excl = block_exclusive_scan((na << 16) | nb, sh, kRedEmit, total);
+  uint32_t oa = excl >> 16, ob = excl & 0xFFFFu;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int t = i * kThreads + (int)threadIdx.x;
@@ -357,6 +383,7 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
       ++ob;
     }
   }
+  if (threadIdx.x == 0) sh.n_out = total >> 16;
   __syncthreads();
   if (!whole) {
     // Key bins fix the top 12 bits of e; linear or single bins fix none.
@@ -426,9 +453,10 @@ __global__ __launch_bounds__(kThreads) void topk_schedule_kernel(Params p) {
     const uint32_t is_short = in && nv > p.k && nv <= kChunk;
     const uint32_t is_triv = in && nv <= p.k;
     const uint32_t nch = is_long ? (uint32_t)((nv + kChunk - 1) / kChunk) : 0u;
-    const uint32_t el = block_exclusive_scan(is_long | (is_short << 16), sh);  // < 2^16 each
-    const uint32_t et = block_exclusive_scan(is_triv, sh);
-    const uint32_t ec = block_exclusive_scan(nch, sh);
+    uint32_t tl, tt, tc;
+    const uint32_t el = block_exclusive_scan(is_long | (is_short << 16), sh, kRedLo, tl);  // < 2^16 each
+    const uint32_t et = block_exclusive_scan(is_triv, sh, kRedHi, tt);
+    const uint32_t ec = block_exclusive_scan(nch, sh, kRedBad, tc);
     if (is_long) {
       const uint32_t slot = off_l + (el & 0xFFFFu);
       p.long_rows[slot] = (uint32_t)r;
@@ -442,17 +470,11 @@ __global__ __launch_bounds__(kThreads) void topk_schedule_kernel(Params p) {
     }
     if (is_short) p.short_rows[off_s + (el >> 16)] = (uint32_t)r;
     if (is_triv) p.triv_rows[off_t + et] = (uint32_t)r;
-    if (threadIdx.x == kThreads - 1) {
-      sh.base_a = el + (is_long | (is_short << 16));
-      sh.base_b = et + is_triv;
-      sh.item = ec + nch;
-    }
-    __syncthreads();
-    off_l += sh.base_a & 0xFFFFu;
-    off_s += sh.base_a >> 16;
-    off_t += sh.base_b;
-    off_c += sh.item;
-    __syncthreads();
+    off_l += tl & 0xFFFFu;
+    off_s += tl >> 16;
+    off_t += tt;
+    off_c += tc;
+    __syncthreads();  // the scratch slots are reused by the next block of rows
   }
   uint2* gh = reinterpret_cast<uint2*>(p.hist);
   const int64_t words2 = (int64_t)off_l * (kKeyBins / 2);
