@@ -124,22 +124,45 @@ struct Stage {
   int phys[kTilesPerStage];
 };
 
-// Exclusive scan of one int per thread over the workgroup (thread order).
-__device__ int block_exclusive_scan(int v, int* wave_tot) {
+// x summed over the four lane groups {c, c+16, c+32, c+48}; every lane gets the sum
+// ((x0 + x2) + (x1 + x3), the same order in every lane).
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then row broadcasts).
+__device__ __forceinline__ uint32_t wave_scan_add(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Exclusive prefix sums of two values per thread over the workgroup (thread order),
+// through red[2 * kWavesPerGroup]. One barrier.
+__device__ __forceinline__ void block_scan2(uint32_t v0, uint32_t v1, uint32_t& e0, uint32_t& e1, uint32_t* red) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
+  const uint32_t i0 = wave_scan_add(v0), i1 = wave_scan_add(v1);
+  if (lane == kWave - 1) {
+    red[wave] = i0;
+    red[kWavesPerGroup + wave] = i1;
   }
-  if (lane == kWave - 1) wave_tot[wave] = incl;
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_tot[w];
-  __syncthreads();
-  return before + incl - v;
+  uint32_t b0 = 0, b1 = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerGroup; ++w) {
+    b0 += w < wave ? red[w] : 0u;
+    b1 += w < wave ? red[kWavesPerGroup + w] : 0u;
+  }
+  e0 = b0 + i0 - v0;
+  e1 = b1 + i1 - v1;
 }
 
 // Largest index i in [0, n) with a[i] <= x (a nondecreasing, a[0] <= x).
@@ -165,10 +188,10 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   int* ctx_s = lds;                     // [B]
   int* stage_pref = lds + B;            // [B+1]
   int* tail_pref = stage_pref + B + 1;  // [B+1]
-  int* scan_tmp = tail_pref + B + 1;    // [kWavesPerGroup]
+  int* scan_tmp = tail_pref + B + 1;    // [2 * kWavesPerGroup]
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4;   // lane group: k-slice for operands, row quad for results
   const int c = lane & 15;   // column (token) / row (head) within a 16-wide tile
   const int L = p.L;
@@ -192,9 +215,9 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         chunks += nc;
       }
     }
-    const int s_excl = block_exclusive_scan(stages, scan_tmp);
-    const int c_excl = block_exclusive_scan(chunks, scan_tmp);
-    int s_run = s_excl, c_run = c_excl;
+    uint32_t s_excl, c_excl;
+    block_scan2((uint32_t)stages, (uint32_t)chunks, s_excl, c_excl, reinterpret_cast<uint32_t*>(scan_tmp));
+    int s_run = (int)s_excl, c_run = (int)c_excl;
     for (int i = 0; i < per; ++i) {
       const int b = r0 + i;
       if (b < B) {
@@ -249,9 +272,6 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
       auto load_table = [&](int st) -> int {
         return btb[st < nstage ? min(t0 + st * kStage + lane, wmax) : 0];
       };
-      int tab0 = load_table(0);
-      int tab1 = load_table(1);
-
       // Query rows of this segment: raw bytes now, f16 A operands once the first key
       // gathers are on their way (the conversion then overlaps their latency).
       i32x4 qraw[TILES][2];
@@ -261,18 +281,18 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         const float* wb = p.w + ((int64_t)b * p.N + j0) * p.H;
 #pragma unroll
         for (int m = 0; m < TILES; ++m) {
-          const bool live = (m / TPJ) < jn;  // wave-uniform
-          const uint8_t* qr = qb + (m * 16 + c) * kD;
-          qraw[m][0] = i32x4{0, 0, 0, 0};
-          qraw[m][1] = i32x4{0, 0, 0, 0};
-          wv[m] = f32x4{0, 0, 0, 0};
-          if (live) {
-            qraw[m][0] = load16(qr + 16 * g);
-            qraw[m][1] = load16(qr + 64 + 16 * g);
-            wv[m] = *reinterpret_cast<const f32x4*>(wb + m * 16 + 4 * g);
-          }
+          // Row tiles of decode rows past N repeat the last row (never stored).
+          const int mr = min(m / TPJ, jn - 1) * TPJ + m % TPJ;
+          const uint8_t* qr = qb + (mr * 16 + c) * kD;
+          qraw[m][0] = load16(qr + 16 * g);
+          qraw[m][1] = load16(qr + 64 + 16 * g);
+          wv[m] = *reinterpret_cast<const f32x4*>(wb + mr * 16 + 4 * g);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      int tab0 = load_table(0);
+      int tab1 = load_table(1);
+      __builtin_amdgcn_sched_barrier(0);
       Operand qa[TILES];
 
       auto issue_keys = [&](int st, int tab, Stage& s) {
@@ -329,8 +349,7 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
               for (int v = 0; v < 4; ++v)
                 part = __builtin_fmaf(wv[m][v], __builtin_elementwise_maximum(acc[m][v], 0.0f), part);
             }
-            part += __shfl_xor(part, 16);
-            part += __shfl_xor(part, 32);
+            part = sum_lane_groups(part);
             if (g == u) keep[jl] = part * sabs;
           }
         }
@@ -345,20 +364,24 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
       // Software pipeline: keys of two stages in flight, table entries two stages ahead
       // of their use; the compute of stage s waits only for stage s's loads, and its
       // registers are refilled with stage s+2 right after.
+      // The prologue issues in the loop's order (keys of a stage, then the table entries
+      // two stages on), so the wait counts computed for the loop's first pass hold for
+      // every pass; stages past the segment issue harmless loads of row 0, so the loop
+      // body is straight-line code. sched_barrier(0) keeps the scheduler from pulling a
+      // use of a load up next to it, which would serialise the latencies.
       Stage sa, sb;
       issue_keys(0, tab0, sa);
-      issue_keys(1, tab1, sb);
       tab0 = load_table(2);
+      issue_keys(1, tab1, sb);
       tab1 = load_table(3);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int m = 0; m < TILES; ++m) qa[m] = to_operand(qraw[m][0], qraw[m][1]);
       for (int st = 0; st < nstage; st += 2) {
         compute_store(st, sa);
-        if (st + 1 >= nstage) break;
         issue_keys(st + 2, tab0, sa);
         tab0 = load_table(st + 4);
-        compute_store(st + 1, sb);
-        if (st + 2 >= nstage) break;
+        if (st + 1 < nstage) compute_store(st + 1, sb);
         issue_keys(st + 3, tab1, sb);
         tab1 = load_table(st + 5);
       }
@@ -369,29 +392,44 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
     }
   }
 
-  // ---- -inf tail: positions past each request's last key stage, every row.
+  // ---- -inf tail: positions past each request's last key stage, every row. Each wave
+  // takes a contiguous run of 1 KB chunks and walks it row by row (LDS is read only
+  // where the run enters another request).
   {
     const int C = tail_pref[B];
-    int ci = (int)((int64_t)gw * C / nwaves);
-    const int ce = (int)((int64_t)(gw + 1) * C / nwaves);
-    int b = ci < ce ? locate(tail_pref, B, ci) : 0;
-    const f32x4 ninf = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-    for (; ci < ce; ++ci) {
-      while (tail_pref[b + 1] <= ci) ++b;
-      const int tail0 = ((ctx_s[b] + kStage - 1) / kStage) * kStage;
-      const int per_row = (L - tail0 + kTailChunk - 1) / kTailChunk;
-      const int local = ci - tail_pref[b];
-      const int j = local / per_row;
-      const int start = tail0 + (local - j * per_row) * kTailChunk;
-      const int end = min(start + kTailChunk, L);
-      float* rp = p.out + (int64_t)(b * p.N + j) * L;
-      const int pos = start + 4 * lane;
-      if (p.vec_store && pos + 4 <= end) {
-        *reinterpret_cast<f32x4*>(rp + pos) = ninf;
-      } else {
+    int ci = __builtin_amdgcn_readfirstlane((int)((int64_t)gw * C / nwaves));
+    const int ce = __builtin_amdgcn_readfirstlane((int)((int64_t)(gw + 1) * C / nwaves));
+    if (ci < ce) {
+      const f32x4 ninf = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+      int b = __builtin_amdgcn_readfirstlane(locate(tail_pref, B, ci));
+      int tail0 = 0, per_row = 1, j = 0, k = 0;
+      auto enter = [&](int local) {  // request b, chunk `local` of its N rows
+        tail0 = __builtin_amdgcn_readfirstlane(((ctx_s[b] + kStage - 1) / kStage) * kStage);
+        per_row = (L - tail0 + kTailChunk - 1) / kTailChunk;
+        j = local / per_row;
+        k = local - j * per_row;
+      };
+      enter(ci - __builtin_amdgcn_readfirstlane(tail_pref[b]));
+      for (;;) {
+        float* rp = p.out + (int64_t)(b * p.N + j) * L;
+        const int start = tail0 + k * kTailChunk;
+        const int end = min(start + kTailChunk, L);
+        const int pos = start + 4 * lane;
+        if (p.vec_store && pos + 4 <= end) {
+          __builtin_nontemporal_store(ninf, reinterpret_cast<f32x4*>(rp + pos));
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (pos + i < end) rp[pos + i] = -__builtin_inff();
+          for (int i = 0; i < 4; ++i)
+            if (pos + i < end) rp[pos + i] = -__builtin_inff();
+        }
+        if (++ci >= ce) break;
+        if (++k == per_row) {
+          k = 0;
+          if (++j == p.N) {  // the next request that has a tail
+            while (b + 1 < B && __builtin_amdgcn_readfirstlane(tail_pref[b + 1]) <= ci) ++b;
+            enter(ci - __builtin_amdgcn_readfirstlane(tail_pref[b]));
+          }
+        }
       }
     }
   }
@@ -428,7 +466,7 @@ int compute_units() {
   return n;
 }
 
-size_t logits_lds_bytes(int32_t batch) { return (size_t)(3 * (int64_t)batch + 2 + kWavesPerGroup) * 4; }
+size_t logits_lds_bytes(int32_t batch) { return (size_t)(3 * (int64_t)batch + 2 + 2 * kWavesPerGroup) * 4; }
 
 }  // namespace
 
