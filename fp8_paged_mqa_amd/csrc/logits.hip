@@ -15,7 +15,8 @@
 //     v_mfma_f32_16x16x32_f16, four chained per 128-wide row: f16 products of e4m3
 //     values are exact and the fp32 accumulation is correctly rounded.
 //   * Schedule: one round of persistent workgroups (CUs x occupancy), so no workgroup
-//     waits for a slot. Each workgroup scans context_lens into LDS prefix sums; every
+//     waits for a slot. Each workgroup scans context_lens into LDS prefix sums (DPP wave
+//     scans, one barrier); every
 //     wave then takes an equal contiguous share of all 64-token key stages of all
 //     requests (split at request boundaries into segments), and afterwards an equal
 //     share of the 1 KB chunks of -inf tail that lie past each request's last stage.
@@ -37,17 +38,19 @@
 //     flight (~17 KB), the table entries two stages ahead of their use, and issues its
 //     first two stages before converting its query rows. Every gather is issued
 //     unconditionally (a dead stage or a table entry outside the cache reads row 0
-//     instead), so the loop is straight-line code and each compute waits only for its
-//     own stage's loads.
+//     instead), and the prologue issues in the loop's order, so the loop is
+//     straight-line code and each compute waits only for its own stage's loads.
 //   * Epilogue in registers: the dequant scale's sign is folded into the fp8 key (flip
 //     the sign bit of every byte, exact; skipped when no scale of the tile is negative),
 //     so relu(scale*s) = |scale| * relu(sign*s) and |scale| multiplies once per token
 //     after the head sum. Each lane sums w * relu over its 4 heads per row tile and the
-//     row tiles of a decode row; two xor-shuffles finish the sum across the 4 lane
-//     groups of a column.
+//     row tiles of a decode row; two cross-lane swaps (v_permlane32_swap, then
+//     v_permlane16_swap) finish the sum across the 4 lane groups of a column.
 //   * Stores: after a 64-token stage each lane group keeps one 16-token column tile, so
 //     a row's 64 logits leave in one 256-byte store; positions past a row's causal limit
-//     inside its last stage are written with -inf there.
+//     inside its last stage are written with -inf there. The -inf tail past the last
+//     stage (most of the output when L >> ctx) is streamed with nontemporal 16-byte
+//     stores: nothing reads it back soon, and the write rate rises from ~4.0 to ~5.5 TB/s.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
