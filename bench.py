@@ -1,6 +1,6 @@
 """Throughput of the fp8 paged MQA indexer (logits + top-2048) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 1..5] [--block-size S] [--no-cpu-baseline]
 
 One step = mqa_paged_logits + mqa_topk over one batch of the named synthetic workload,
 inputs already resident in HBM. Steps are captured into a HIP graph and replayed (the
@@ -47,8 +47,9 @@ def algorithmic_bytes(w):
     sum_ctx = w.sum_ctx
     rows = w.rows
     nv = w.visible().astype(np.int64)
+    blocks = int(((w.context_lens.astype(np.int64) + w.block_size - 1) // w.block_size).sum())
     logits = (ROW_BYTES * sum_ctx            # key rows + scales
-              + 4 * sum_ctx                  # block-table entries
+              + 4 * blocks                   # block-table entries (one per block)
               + w.q.nbytes + w.weights.nbytes + 4 * w.batch
               + 4 * rows * w.max_model_len)  # every logit slot, -inf tail included
     topk = 4 * int(nv[nv > w.k].sum()) + 4 * rows * w.k + 4 * w.batch
@@ -101,6 +102,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--block-size", type=int, default=1,
+                    help="tokens per KV block (1: the pages' layout; the default line uses 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=256,
                     help="size of the plain device copy run once for counter calibration (0: skip)")
@@ -114,10 +117,11 @@ def main():
     sys.path.insert(0, ROOT)
     from fp8_paged_mqa_amd import mqa, workloads
 
-    w = workloads.make_config(args.config, poison_unused=False)
+    w = workloads.make_config(args.config, poison_unused=False, block_size=args.block_size)
     print(f"[bench] {w.name}: sum_ctx={w.sum_ctx} pool={w.num_blocks}", file=sys.stderr, flush=True)
     dev = "cuda"
-    shape = mqa.make_shape(w.batch, w.next_n, w.heads, w.num_blocks, w.block_tables.shape[1])
+    shape = mqa.make_shape(w.batch, w.next_n, w.heads, w.num_blocks, w.block_tables.shape[1],
+                           block_size=w.block_size)
     L, k = w.max_model_len, w.k
     C = max(1, args.copies)
     ws_bytes = max(1, mqa.mqa_topk_workspace_bytes(shape, L, k))
@@ -208,7 +212,8 @@ def main():
 
     bytes_logits, bytes_topk = algorithmic_bytes(w)
     achieved = bytes_logits / (t_logits * 1e-6) / 1e9
-    traffic = traffic_from_profile("logits", f"config{args.config}", source_digest(LOGITS_SRC))
+    tag = f"config{args.config}" + (f"_bs{w.block_size}" if w.block_size > 1 else "")
+    traffic = traffic_from_profile("logits", tag, source_digest(LOGITS_SRC))
     value = w.sum_ctx / (ms_per_step * 1e-3)
     step_gbps = (bytes_logits + bytes_topk) / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -225,7 +230,7 @@ def main():
         "dtype": "fp8e4m3fn->f16 mfma, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "next_n": w.next_n, "heads": w.heads,
-                   "head_dim": 128, "block_size": 1, "max_model_len": L, "k": k,
+                   "head_dim": 128, "block_size": w.block_size, "max_model_len": L, "k": k,
                    "sum_ctx": w.sum_ctx, "pool_rows": w.num_blocks, "input_copies": C,
                    "timing": "HIP graph replay of the step"},
         "hbm_frac_step": step_gbps / HBM_PEAK_GBPS,

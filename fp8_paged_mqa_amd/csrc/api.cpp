@@ -12,6 +12,13 @@ constexpr int32_t kHeadDim = 128;
 constexpr int32_t kMaxTopk = 2048;
 constexpr int32_t kMaxModelLen = 1 << 30;
 constexpr int32_t kMaxBatch = 8192;  // the logits schedule keeps 3 ints per request in LDS
+constexpr int32_t kMaxBlockSize = 1 << 16;
+
+int32_t log2_exact(int32_t v) {
+  int32_t s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -23,7 +30,10 @@ int check_shape(const mqa_shape* s, int32_t max_model_len) {
       s->block_table_stride < 1 || s->num_blocks < 1 || max_model_len < 1)
     return MQA_ERR_SHAPE;
   if ((int64_t)s->batch * s->next_n > INT32_MAX) return MQA_ERR_SHAPE;
-  if (s->head_dim != kHeadDim || s->block_size != 1) return MQA_ERR_UNSUPPORTED;
+  if (s->head_dim != kHeadDim) return MQA_ERR_UNSUPPORTED;
+  if (s->block_size > kMaxBlockSize || (s->block_size & (s->block_size - 1)) != 0) return MQA_ERR_UNSUPPORTED;
+  if ((int64_t)s->block_table_stride * s->block_size > INT32_MAX) return MQA_ERR_UNSUPPORTED;
+  if (s->block_size > 1 && s->num_blocks > INT32_MAX / s->block_size) return MQA_ERR_UNSUPPORTED;
   if (s->heads % 16 != 0 || s->heads > 128) return MQA_ERR_UNSUPPORTED;
   if (s->next_n > 4) return MQA_ERR_UNSUPPORTED;
   if (max_model_len > kMaxModelLen) return MQA_ERR_UNSUPPORTED;
@@ -40,7 +50,9 @@ const char* mqa_status_string(int status) {
     case MQA_ERR_NULL: return "a required pointer is NULL";
     case MQA_ERR_SHAPE: return "invalid shape or size";
     case MQA_ERR_UNSUPPORTED:
-      return "unsupported: needs head_dim 128, block_size 1, heads a multiple of 16 up to 128, "
+      return "unsupported: needs head_dim 128, block_size a power of two up to 65536 (with "
+             "block_table_stride * block_size and, for block_size > 1, num_blocks * block_size "
+             "below 2^31), heads a multiple of 16 up to 128, "
              "next_n 1..4, max_model_len <= 2^30, batch <= 8192 for the logits, k 1..2048, 16-byte aligned q and weights, "
              "4-byte aligned kv_cache, logits, idx and integer arrays";
     case MQA_ERR_WORKSPACE: return "workspace missing or too small";
@@ -74,6 +86,7 @@ int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* wei
   a.heads = shape->heads;
   a.bt_stride = shape->block_table_stride;
   a.max_model_len = max_model_len;
+  a.block_shift = log2_exact(shape->block_size);
   return mqa::launch_logits(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
@@ -102,7 +115,7 @@ int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model
   a.workspace = workspace;
   a.batch = shape->batch;
   a.next_n = shape->next_n;
-  a.bt_stride = shape->block_table_stride;
+  a.token_capacity = shape->block_table_stride * shape->block_size;
   a.max_model_len = max_model_len;
   a.k = k;
   return mqa::launch_topk(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;

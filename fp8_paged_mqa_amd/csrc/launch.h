@@ -18,6 +18,7 @@ struct LogitsLaunch {
   float* out;
   int64_t num_blocks;
   int32_t batch, next_n, heads, bt_stride, max_model_len;
+  int32_t block_shift;  // log2(block_size)
 };
 
 struct TopkLaunch {
@@ -25,7 +26,8 @@ struct TopkLaunch {
   const int32_t* ctx_lens;
   int32_t* idx;
   void* workspace;  // topk_workspace_bytes(rows, max_model_len) bytes, 8-byte aligned
-  int32_t batch, next_n, bt_stride, max_model_len, k;
+  int32_t batch, next_n, max_model_len, k;
+  int32_t token_capacity;  // block_table_stride * block_size: tokens a table row can address
 };
 
 // Device scratch the top-k launch needs for `rows` rows of length max_model_len

@@ -4,8 +4,9 @@
 //   logit = sum_h w[r,h] * relu(scale_t * (q[b,j,h,:] . k_t))   if t <= ctx_b - N + j
 //   -inf                                                        otherwise,
 // where k_t / scale_t are the 128 e4m3fn bytes and the fp32 of the 132-byte cache row
-// that the block table maps t to (block_size 1). Definition: stepcodex.com issue
-// "[Bug] aiter ops triton attention pa_mqa_logits", section "Minimal reproduction".
+// of token t: slot t % S of block block_tables[b][t / S], S = block_size (a power of
+// two). Definition: stepcodex.com issue "[Bug] aiter ops triton attention
+// pa_mqa_logits", section "Minimal reproduction".
 //
 // Mapping onto CDNA4
 //   * Precision: gfx950's fp8 MFMAs (16x16x128 f8f6f4 and 16x16x32 fp8) round the dot
@@ -33,8 +34,9 @@
 //     instruction covers the first (then the second) 64 contiguous bytes of 16 rows. A
 //     and B use the same byte-to-k assignment, so the contraction covers all 128 k
 //     whatever order the hardware uses internally.
-//   * The block table is read 64 tokens at a time (one coalesced dword per lane) and
-//     redistributed with ds_bpermute. A wave keeps the keys of two 64-token stages in
+//   * The block table is read 64 tokens at a time (lane l reads the entry of token
+//     t0 + l: one coalesced dword per lane for S = 1, a broadcast for S >= 64) and
+//     redistributed with ds_bpermute; the row is entry * S + t % S. A wave keeps the keys of two 64-token stages in
 //     flight (~17 KB), the table entries two stages ahead of their use, and issues its
 //     first two stages before converting its query rows. Every gather is issued
 //     unconditionally (a dead stage or a table entry outside the cache reads row 0
@@ -80,8 +82,10 @@ struct Params {
   const int32_t* ctx_lens;
   const int32_t* bt;
   float* out;
-  uint32_t nblk;      // valid physical rows are [0, nblk) (num_blocks capped at 2^31 - 1)
-  int32_t B, N, H, W, L;
+  uint32_t nblk;      // valid block ids are [0, nblk) (num_blocks capped at 2^31 - 1)
+  int32_t B, N, H, W, L;  // W: block-table row length, in blocks
+  int32_t bshift;     // log2(block_size)
+  int32_t Wt;         // W << bshift: tokens a table row can address
   int32_t groups;     // row groups: waves that walk the same stages for different rows
   int32_t vec_store;  // rows of `out` are 16-byte aligned (L % 4 == 0, aligned base)
 };
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
     for (int i = 0; i < per; ++i) {
       const int b = r0 + i;
       if (b < B) {
-        const int ctx = max(0, min(p.ctx_lens[b], min(p.W, L)));
+        const int ctx = max(0, min(p.ctx_lens[b], min(p.Wt, L)));
         const int ns = (ctx + kStage - 1) / kStage;
         const int tail0 = ns * kStage;
         const int nc = tail0 < L ? p.N * ((L - tail0 + kTailChunk - 1) / kTailChunk) : 0;
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
       const int32_t* btb = p.bt + (int64_t)b * p.W;
       const int wmax = p.W - 1;
       auto load_table = [&](int st) -> int {
-        return btb[st < nstage ? min(t0 + st * kStage + lane, wmax) : 0];
+        return btb[st < nstage ? min((t0 + st * kStage + lane) >> p.bshift, wmax) : 0];
       };
       // Query rows of this segment: raw bytes now, f16 A operands once the first key
       // gathers are on their way (the conversion then overlaps their latency).
@@ -303,9 +307,12 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         int ph[kTilesPerStage];
 #pragma unroll
         for (int u = 0; u < kTilesPerStage; ++u) ph[u] = __shfl(tab, u * 16 + c);
+        const uint32_t smask = (1u << p.bshift) - 1u;  // slot of a token in its block
+        const uint32_t tok = (uint32_t)(t0 + st * kStage + c);
 #pragma unroll
         for (int u = 0; u < kTilesPerStage; ++u) {
-          const uint32_t row = (live && (uint32_t)ph[u] < p.nblk) ? (uint32_t)ph[u] : 0u;
+          const uint32_t slot = (tok + 16u * u) & smask;
+          const uint32_t row = (live && (uint32_t)ph[u] < p.nblk) ? ((uint32_t)ph[u] << p.bshift) | slot : 0u;
           const uint8_t* kp = kv_g + (uint64_t)row * kRow;
           s.phys[u] = ph[u];
           s.lo[u] = load16(kp);
@@ -490,6 +497,8 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   p.H = a.heads;
   p.W = a.bt_stride;
   p.L = a.max_model_len;
+  p.bshift = a.block_shift;
+  p.Wt = a.bt_stride << a.block_shift;
   p.groups = (a.next_n + jpg - 1) / jpg;
   p.vec_store = (a.max_model_len % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
   KernelFn fn = kTable[tpj - 1][jpg - 1];

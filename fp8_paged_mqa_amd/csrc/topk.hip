@@ -624,7 +624,7 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
   p.idx = a.idx;
   p.rows = (int32_t)rows;
   p.N = a.next_n;
-  p.W = a.bt_stride;
+  p.W = a.token_capacity;
   p.L = a.max_model_len;
   p.k = a.k;
   if (a.max_model_len <= kChunk) {  // every row fits one workgroup

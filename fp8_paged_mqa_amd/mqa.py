@@ -59,10 +59,11 @@ def make_shape(batch, next_n, heads, num_blocks, block_table_stride, head_dim=12
 
 def shape_of(q: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tensor) -> mqa_shape:
     """Shape struct from tensors laid out as the header describes: q [B,N,H,D],
-    kv_cache [num_blocks, (block_size, 1,) D+4], block_tables [B, W]."""
+    kv_cache [num_blocks, D+4] (block_size 1) or [num_blocks, block_size, (1,) D+4],
+    block_tables [B, W]."""
     B, N, H, D = q.shape
     return make_shape(B, N, H, kv_cache.shape[0], block_tables.shape[1], head_dim=D,
-                      block_size=kv_cache.shape[1] if kv_cache.dim() == 4 else 1)
+                      block_size=kv_cache.shape[1] if kv_cache.dim() >= 3 else 1)
 
 
 def _ptr(t):

@@ -12,9 +12,11 @@ issue "[Bug] aiter ops triton attention pa_mqa_logits", section "Minimal
 reproduction"):
   q             uint8 [B, N, H, 128]   e4m3fn
   kv_cache      uint8 [num_blocks, 132] 128 e4m3fn key bytes + fp32 scale (LE)
+                      ([num_blocks, block_size, 132] for block_size > 1)
   weights       f32   [B*N, H]
   context_lens  i32   [B]
-  block_tables  i32   [B, W]           slots t >= ctx hold -1
+  block_tables  i32   [B, W]           block of token t: entry t // block_size;
+                                       entries past the last block hold -1
 """
 from __future__ import annotations
 
@@ -58,6 +60,10 @@ class Workload:
         return int(self.kv_cache.shape[0])
 
     @property
+    def block_size(self) -> int:
+        return 1 if self.kv_cache.ndim == 2 else int(self.kv_cache.shape[1])
+
+    @property
     def sum_ctx(self) -> int:
         return int(self.context_lens.astype(np.int64).sum())
 
@@ -99,16 +105,24 @@ def _tables_from_assignment(ctx: np.ndarray, width: int, assign) -> np.ndarray:
 
 def build(name, rng, *, batch, next_n, heads, ctx, max_model_len, pool, table,
           table_width=None, outlier_frac=0.0, poison_unused=True, k=TOPK,
-          key_fn=None, scale_fn=None, q_fn=None, w_fn=None) -> Workload:
+          key_fn=None, scale_fn=None, q_fn=None, w_fn=None, block_size=1) -> Workload:
     """Draws a workload in the fixed order ctx -> tables -> q -> K -> scales ->
     outliers -> weights. ``ctx`` is an int array already drawn by the caller.
 
-    table: "identity"  request b reads rows [0, ctx_b) (every request the same)
+    table: "identity"  request b reads blocks [0, n_b) (every request the same)
            "permuted"  one permutation of the pool, sliced per request in order
-           "interleaved" one permutation, dealt out token by token across the
-                       requests still running (for t, for b with ctx_b > t)
+           "interleaved" one permutation, dealt out block by block across the
+                       requests still running (for i, for b with n_b > i)
+    where n_b = ceil(ctx_b / block_size) and the pool counts blocks. With
+    block_size > 1 the cache is [pool, block_size, 132] and ``table_width``
+    counts blocks.
     """
     ctx = np.asarray(ctx, dtype=np.int32)
+    bs = int(block_size)
+    if bs > 1:
+        return _build_blocked(name, rng, batch=batch, next_n=next_n, heads=heads, ctx=ctx,
+                              max_model_len=max_model_len, pool=pool, table=table,
+                              table_width=table_width, poison_unused=poison_unused, k=k, bs=bs)
     width = int(table_width or max(1, int(ctx.max(initial=1))))
     if table == "identity":
         bt = _tables_from_assignment(ctx, width, lambda b, c: np.arange(c))
@@ -152,6 +166,45 @@ def build(name, rng, *, batch, next_n, heads, ctx, max_model_len, pool, table,
                     meta={"table": table, "pool": int(pool)})
 
 
+def _build_blocked(name, rng, *, batch, next_n, heads, ctx, max_model_len, pool, table,
+                   table_width, poison_unused, k, bs) -> Workload:
+    """build() for block_size > 1: tables of block ids, cache [pool, bs, 132]."""
+    nblk = (ctx.astype(np.int64) + bs - 1) // bs
+    width = int(table_width or max(1, int(nblk.max(initial=1))))
+    if table == "identity":
+        bt = _tables_from_assignment(nblk, width, lambda b, n: np.arange(n))
+    elif table == "permuted":
+        perm = rng.permutation(pool).astype(np.int32)
+        offs = np.concatenate([[0], np.cumsum(nblk)])
+        assert offs[-1] <= pool, "pool smaller than the blocks in use"
+        bt = _tables_from_assignment(nblk, width, lambda b, n: perm[offs[b]:offs[b] + n])
+    elif table == "interleaved":
+        perm = rng.permutation(pool).astype(np.int32)
+        b_idx = np.repeat(np.arange(nblk.size), nblk)
+        i_idx = np.concatenate([np.arange(n) for n in nblk.tolist()]) if nblk.size else np.zeros(0, int)
+        order = np.lexsort((b_idx, i_idx))
+        assert order.size <= pool
+        bt = np.full((nblk.size, width), -1, dtype=np.int32)
+        bt[b_idx[order], i_idx[order]] = perm[:order.size]
+    else:
+        raise ValueError(table)
+    rows = batch * next_n
+    q_f = rng.standard_normal((batch, next_n, heads, HEAD_DIM), dtype=np.float32)
+    k_f = rng.standard_normal((pool * bs, HEAD_DIM), dtype=np.float32)
+    scales = rng.lognormal(0.0, 0.5, size=pool * bs).astype(np.float32)
+    weights = rng.standard_normal((rows, heads), dtype=np.float32)
+    kv = _kv_rows(to_e4m3fn_bytes(k_f), scales)
+    if poison_unused:  # every row that no token t < ctx reads
+        used = np.concatenate([bt[b, np.arange(c) // bs].astype(np.int64) * bs + np.arange(c) % bs
+                               for b, c in enumerate(ctx.tolist())] + [np.zeros(0, np.int64)])
+        _poison_rows(kv, used)
+    return Workload(name=name, q=to_e4m3fn_bytes(q_f), kv_cache=kv.reshape(pool, bs, ROW_BYTES),
+                    weights=np.ascontiguousarray(weights, dtype=np.float32),
+                    context_lens=ctx, block_tables=bt, max_model_len=int(max_model_len),
+                    next_n=int(next_n), k=int(k),
+                    meta={"table": table, "pool": int(pool), "block_size": bs})
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.
 # ---------------------------------------------------------------------------
@@ -164,9 +217,15 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(n: int, *, poison_unused: bool = True, seed: int | None = None) -> Workload:
+def make_config(n: int, *, poison_unused: bool = True, seed: int | None = None,
+                block_size: int = 1) -> Workload:
+    """The named workload n. With block_size S > 1 the same context lengths are laid
+    out in blocks of S tokens: the pool becomes ceil(rows / S) blocks (at least the
+    blocks in use) and the table kind is kept; keys and scales are drawn afresh."""
     rng = np.random.Generator(np.random.PCG64(42 + (n - 1) if seed is None else seed))
     name = f"config{n}: {CONFIG_NAMES[n]}"
+    if block_size > 1:
+        return _make_config_blocked(n, rng, name, poison_unused, int(block_size))
     if n == 1:
         ctx = np.array([2049])
         return build(name, rng, batch=1, next_n=1, heads=32, ctx=ctx, max_model_len=4096,
@@ -196,14 +255,44 @@ def make_config(n: int, *, poison_unused: bool = True, seed: int | None = None) 
     raise ValueError(n)
 
 
+def _make_config_blocked(n, rng, name, poison_unused, bs) -> Workload:
+    # Same context-length draws as make_config's block_size 1 path.
+    if n == 1:
+        ctx, kw = np.array([2049]), dict(batch=1, next_n=1, heads=32, max_model_len=4096, rows=2065,
+                                         table="identity")
+    elif n == 2:
+        ctx = rng.integers(1, 8192, size=64, endpoint=True)
+        ctx[:5] = [2047, 2048, 2049, 4096, 4097]
+        kw = dict(batch=64, next_n=1, heads=64, max_model_len=8192, rows=600_000, table="permuted")
+    elif n == 3:
+        ctx = rng.integers(2048, 32768, size=32, endpoint=True)
+        kw = dict(batch=32, next_n=2, heads=64, max_model_len=32768, rows=int(ctx.sum()), table="permuted")
+    elif n == 4:
+        ctx = np.array([65536, 131071, 131072, 202752])
+        kw = dict(batch=4, next_n=1, heads=64, max_model_len=202752, rows=540_000, table="permuted")
+    elif n == 5:
+        ctx = np.clip(np.round(np.exp(rng.normal(np.log(6000.0), 1.2, size=128))), 4, 202752).astype(np.int64)
+        kw = dict(batch=128, next_n=4, heads=32, max_model_len=202752, rows=int(ctx.sum()), table="interleaved")
+    else:
+        raise ValueError(n)
+    rows = kw.pop("rows")
+    need = int(((np.asarray(ctx, dtype=np.int64) + bs - 1) // bs).sum())
+    pool = max(need, (rows + bs - 1) // bs)
+    return build(f"{name}, block_size {bs}", rng, ctx=ctx, pool=pool, poison_unused=poison_unused,
+                 block_size=bs, **kw)
+
+
 def make_case(*, batch, next_n, heads, ctx, max_model_len=None, seed=0, table="permuted",
-              pool=None, table_width=None, poison_unused=True, k=TOPK, **kw) -> Workload:
-    """A small seeded case (for sweeps and edge cases)."""
+              pool=None, table_width=None, poison_unused=True, k=TOPK, block_size=1, **kw) -> Workload:
+    """A small seeded case (for sweeps and edge cases). ``pool`` counts blocks."""
     rng = np.random.Generator(np.random.PCG64(seed))
     ctx = np.broadcast_to(np.asarray(ctx, dtype=np.int64), (batch,)).copy()
     L = int(max_model_len or max(1, int(ctx.max(initial=1))))
     if pool is None:
-        pool = int(ctx.max(initial=1)) if table == "identity" else max(1, int(ctx.sum()))
+        nblk = (ctx + block_size - 1) // block_size
+        pool = int(nblk.max(initial=1)) if table == "identity" else max(1, int(nblk.sum()))
+    if block_size > 1:
+        kw["block_size"] = block_size
     return build(f"case b{batch} n{next_n} h{heads} seed{seed}", rng, batch=batch,
                  next_n=next_n, heads=heads, ctx=ctx, max_model_len=L, pool=pool, table=table,
                  table_width=table_width, poison_unused=poison_unused, k=k, **kw)

@@ -3,9 +3,10 @@
  *
  * The operation is the decode step of the sparse-attention indexer described on
  * the stepcodex.com issue page "[Bug] aiter ops triton attention pa_mqa_logits"
- * (section "Minimal reproduction": the torch reference function and the
+ * (section "Minimal reproduction": the torch reference function, which reads
+ * block_size from the cache shape and walks the blocks of a request, and the
  * reproducer's top-k comparison; section "Observations while narrowing it down"
- * for block_size 1 and the index head counts).
+ * for the block sizes in use and the index head counts).
  *
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer (hipMalloc or torch CUDA tensor memory),
@@ -20,9 +21,9 @@
  *   - Values that live on the device (context lengths, block-table entries) cannot
  *     be checked on the host. The kernels clamp them so that no access leaves the
  *     buffers described by `shape`:
- *       ctx is read as min(max(ctx, 0), block_table_stride, max_model_len);
- *       a block-table entry outside [0, num_blocks) yields NaN logits for that
- *       token instead of a memory access.
+ *       ctx is read as min(max(ctx, 0), block_table_stride * block_size,
+ *       max_model_len); a block-table entry outside [0, num_blocks) yields NaN
+ *       logits for the tokens of that block instead of a memory access.
  *   - Calls are reentrant: no mutable global state.
  */
 #ifndef MQA_H
@@ -54,9 +55,11 @@ enum {
  *   next_n              N, decode rows per request (speculative depth + 1), 1..4
  *   heads               H, index query heads, a multiple of 16 in [16, 128]
  *   head_dim            D, must be 128
- *   block_size          tokens per KV block, must be 1
- *   block_table_stride  W, int32 elements per block-table row (>= 1)
- *   num_blocks          physical rows in the KV cache (>= 1)
+ *   block_size          S, tokens per KV block: a power of two in [1, 65536]
+ *   block_table_stride  W, int32 elements (blocks) per block-table row (>= 1);
+ *                       W * S <= 2^31 - 1
+ *   num_blocks          blocks in the KV cache (>= 1); for S > 1, num_blocks * S
+ *                       <= 2^31 - 1
  * Row r of the logits and of the indices is decode row j of request b, r = b*N + j.
  */
 typedef struct mqa_shape {
@@ -74,16 +77,18 @@ typedef struct mqa_shape {
  *
  * Definition (stepcodex.com pa_mqa_logits issue, "Minimal reproduction", the torch
  * reference): for row r = b*N + j with context length ctx = context_lens[b], position t
- * is visible iff t <= ctx - N + j (the row's own position; it implies t < ctx). For a
- * visible t with physical row p = block_tables[b*W + t]:
+ * is visible iff t <= ctx - N + j (the row's own position; it implies t < ctx). Token t
+ * is slot t % S of block block_tables[b*W + t / S]; for a visible t that is cache row
+ * p = block_tables[b*W + t / S] * S + t % S, and:
  *     k      = e4m3fn bytes kv_cache[p*132 + 0 .. 127]          (OCP E4M3, bias 7)
  *     scale  = little-endian fp32 at kv_cache[p*132 + 128 .. 131]
  *     out[r*max_model_len + t] = sum_h weights[r*H + h] * relu(scale * (q[b,j,h,:] . k))
  * Every other slot of the row, t in [visible, max_model_len), is written with -inf.
  *
  *   q               uint8  [B, N, H, 128]   e4m3fn, contiguous
- *   kv_cache        uint8  [num_blocks, 132] 128 e4m3fn key bytes, then the fp32 scale;
- *                                            rows are 4-byte aligned (pointer must be too)
+ *   kv_cache        uint8  [num_blocks, S, 132] per token: 128 e4m3fn key bytes, then
+ *                                            the fp32 scale; rows are 4-byte aligned
+ *                                            (the pointer must be too)
  *   weights         float  [B*N, H]
  *   context_lens    int32  [B]
  *   block_tables    int32  [B, W]

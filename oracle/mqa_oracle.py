@@ -15,6 +15,9 @@ and the reproducer's ``test()``.
 * The KV cache row of a token holds D fp8-e4m3fn bytes followed by 4 bytes that
   are read as one fp32 dequant scale. The row is dequantised as fp8 value times
   scale before the dot product.
+* The cache is [num_blocks, block_size, 1, D+4]; the reference reads block_size
+  from that shape and walks a request's blocks: token t is slot t % block_size of
+  block block_tables[b][t // block_size]. The reproducer uses block_size 1.
 * All H query heads of a decode row are dotted with the same dequantised key
   (MQA: the cache has one key head).
 * Decode row j of request b sits at position ctx - N + j, where ctx is the
@@ -83,14 +86,29 @@ def decode_bytes(codes: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Step 2: the cache row. Bytes [0, D) are fp8 key values, bytes [D, D+4) are
 # the per-token fp32 scale, read little-endian (``.view(torch.float32)`` of the
-# trailing bytes in the page's reference). block_size is 1: one row per block.
+# trailing bytes in the page's reference). A block holds block_size such rows.
 # ---------------------------------------------------------------------------
+def block_size_of(kv_cache: np.ndarray) -> int:
+    """block_size of a cache shaped [num_blocks, D+4] (block_size 1),
+    [num_blocks, block_size, D+4] or [num_blocks, block_size, 1, D+4]."""
+    kv = np.asarray(kv_cache)
+    return 1 if kv.ndim == 2 else int(kv.shape[1])
+
+
 def split_kv_rows(kv_cache: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
-    """Returns (key values [num_blocks, D] float64, scales [num_blocks] float64)."""
+    """Returns (key values [num_blocks * block_size, D] float64, scales [...] float64),
+    row blk * block_size + slot."""
     kv = np.asarray(kv_cache, dtype=np.uint8).reshape(-1, ROW_BYTES)
     keys = decode_bytes(kv[:, :HEAD_DIM])
     scales = np.ascontiguousarray(kv[:, HEAD_DIM:ROW_BYTES]).view("<f4")[:, 0]
     return keys, scales.astype(np.float64)
+
+
+def token_rows(table_row: np.ndarray, ctx: int, block_size: int) -> np.ndarray:
+    """Cache row of tokens 0..ctx-1 of one request: slot t % block_size of block
+    table_row[t // block_size]."""
+    t = np.arange(ctx, dtype=np.int64)
+    return np.asarray(table_row)[t // block_size].astype(np.int64) * block_size + t % block_size
 
 
 def visible_count(ctx: int, next_n: int, j: int, max_model_len: int) -> int:
@@ -99,11 +117,11 @@ def visible_count(ctx: int, next_n: int, j: int, max_model_len: int) -> int:
     return max(0, min(ctx - next_n + j + 1, max_model_len))
 
 
-def _check_preconditions(context_lens, block_tables, max_model_len):
+def _check_preconditions(context_lens, block_tables, max_model_len, block_size=1):
     for b, ctx in enumerate(np.asarray(context_lens).tolist()):
-        if ctx < 0 or ctx > max_model_len or ctx > block_tables.shape[1]:
+        if ctx < 0 or ctx > max_model_len or ctx > block_tables.shape[1] * block_size:
             raise ValueError(
-                f"request {b}: context length {ctx} outside [0, min(max_model_len, table width)]")
+                f"request {b}: context length {ctx} outside [0, min(max_model_len, table capacity)]")
 
 
 # ---------------------------------------------------------------------------
@@ -113,16 +131,17 @@ def paged_mqa_logits(q, kv_cache, weights, context_lens, block_tables, max_model
     """Logits [B*N, max_model_len] float64.
 
     q            uint8 [B, N, H, D]   e4m3fn bytes
-    kv_cache     uint8 [num_blocks, D + 4] (block_size 1)
+    kv_cache     uint8 [num_blocks, (block_size, (1,)) D + 4]
     weights      float [B*N, H]
     context_lens int   [B]
-    block_tables int   [B, W]         physical row of logical token t
+    block_tables int   [B, W]         block of logical token t: entry t // block_size
     """
     q = np.asarray(q, dtype=np.uint8)
     B, N, H, D = q.shape
     assert D == HEAD_DIM
     block_tables = np.asarray(block_tables)
-    _check_preconditions(context_lens, block_tables, max_model_len)
+    bs = block_size_of(kv_cache)
+    _check_preconditions(context_lens, block_tables, max_model_len, bs)
     keys, scales = split_kv_rows(kv_cache)
     w = np.asarray(weights, dtype=np.float64).reshape(B * N, H)
     qv = decode_bytes(q)                                   # [B, N, H, D]
@@ -131,7 +150,7 @@ def paged_mqa_logits(q, kv_cache, weights, context_lens, block_tables, max_model
         ctx = int(context_lens[b])
         if ctx <= 0:
             continue
-        phys = block_tables[b, :ctx].astype(np.int64)
+        phys = token_rows(block_tables[b], ctx, bs)
         k_b = keys[phys]                                   # [ctx, D]  key of token t
         s_b = scales[phys]                                 # [ctx]
         for j in range(N):
@@ -153,8 +172,9 @@ def paged_mqa_logit_at(q, kv_cache, weights, context_lens, block_tables, max_mod
     ctx = int(context_lens[b])
     if t < 0 or t >= visible_count(ctx, N, j, max_model_len):
         return -math.inf
+    bs = block_size_of(kv_cache)
     kv = np.asarray(kv_cache, dtype=np.uint8).reshape(-1, ROW_BYTES)
-    phys = int(block_tables[b, t])
+    phys = int(block_tables[b, t // bs]) * bs + t % bs
     key = decode_bytes(kv[phys, :HEAD_DIM])
     scale = float(np.ascontiguousarray(kv[phys, HEAD_DIM:ROW_BYTES]).view("<f4")[0])
     w = np.asarray(weights, dtype=np.float64).reshape(B * N, H)[row]

@@ -41,7 +41,8 @@ def device_inputs(wl):
 
 
 def shape_of(wl):
-    return mqa.make_shape(wl.batch, wl.next_n, wl.heads, wl.num_blocks, wl.block_tables.shape[1])
+    return mqa.make_shape(wl.batch, wl.next_n, wl.heads, wl.num_blocks, wl.block_tables.shape[1],
+                          block_size=wl.block_size)
 
 
 def run_gpu(wl, k=None, poison=True):

@@ -148,7 +148,8 @@ def _exact_logits(case):
             for t in range(L):
                 if not (t < ctx and t <= ctx - N + j):
                     continue
-                row = case.kv_cache[int(case.block_tables[b, t])]
+                bs = case.block_size  # token t: slot t % bs of block table[t // bs]
+                row = case.kv_cache.reshape(-1, 132)[int(case.block_tables[b, t // bs]) * bs + t % bs]
                 scale = Fraction(struct.unpack("<f", row[128:132].tobytes())[0])
                 total = Fraction(0)
                 terms = Fraction(0)
@@ -164,9 +165,11 @@ def _exact_logits(case):
 
 
 def pin_exact_rationals(orc):
-    for seed, (B, N, H, ctxs) in enumerate([(1, 1, 1, [5]), (2, 2, 3, [4, 6]), (2, 1, 4, [1, 3]),
-                                            (1, 3, 2, [6]), (2, 2, 2, [1, 5])]):
-        case = wl.make_case(batch=B, next_n=N, heads=H, ctx=ctxs, max_model_len=7, seed=100 + seed)
+    for seed, (B, N, H, ctxs, bs) in enumerate([(1, 1, 1, [5], 1), (2, 2, 3, [4, 6], 1), (2, 1, 4, [1, 3], 1),
+                                                (1, 3, 2, [6], 1), (2, 2, 2, [1, 5], 1), (2, 2, 2, [5, 3], 2),
+                                                (1, 2, 3, [7], 4)]):
+        case = wl.make_case(batch=B, next_n=N, heads=H, ctx=ctxs, max_model_len=7, seed=100 + seed,
+                            block_size=bs, pool=8 if bs > 1 else None)
         got = orc.paged_mqa_logits(case.q, case.kv_cache, case.weights, case.context_lens,
                                    case.block_tables, case.max_model_len)
         exact = _exact_logits(case)
@@ -246,6 +249,25 @@ def pin_paging_identity(orc):
     assert np.array_equal(out, out2)
 
 
+def pin_block_size_identity(orc):
+    """The same tokens stored in blocks of 16 (permuted blocks, a partly filled last
+    block per request) give exactly the logits of a block_size 1 cache holding each
+    token's row behind a per-token table."""
+    case = wl.make_case(batch=3, next_n=2, heads=32, ctx=[33, 5, 70], max_model_len=80, seed=13,
+                        block_size=16, pool=12)
+    assert case.kv_cache.shape[1] == 16
+    out = orc.paged_mqa_logits(case.q, case.kv_cache, case.weights, case.context_lens,
+                               case.block_tables, case.max_model_len)
+    rows = case.kv_cache.reshape(-1, 132)
+    bt1 = np.full((case.batch, 80), -1, dtype=np.int32)
+    for b in range(case.batch):
+        for t in range(int(case.context_lens[b])):
+            bt1[b, t] = int(case.block_tables[b, t // 16]) * 16 + t % 16
+    out1 = orc.paged_mqa_logits(case.q, rows, case.weights, case.context_lens, bt1, case.max_model_len)
+    assert np.array_equal(out, out1)
+    assert np.isfinite(out).sum() == sum(max(0, int(c) - 2 + j + 1) for c in case.context_lens for j in range(2))
+
+
 def pin_batch_and_length_invariance(orc):
     case = wl.make_case(batch=4, next_n=2, heads=32, ctx=[12, 30, 3, 25], max_model_len=32, seed=12)
     full = orc.paged_mqa_logits(case.q, case.kv_cache, case.weights, case.context_lens,
@@ -311,6 +333,7 @@ def pin_topk_ctx_k_plus_one_drops_argmin(orc):
 
 
 PINS = [
+    pin_block_size_identity,
     pin_decode_matches_torch,
     pin_decode_golden_spot_values,
     pin_decode_structure,

@@ -68,9 +68,12 @@ def good_shape(**kw):
     (dict(block_table_stride=0), 100, mqa.MQA_ERR_SHAPE),
     ({}, 0, mqa.MQA_ERR_SHAPE),
     (dict(head_dim=64), 100, mqa.MQA_ERR_UNSUPPORTED),
-    (dict(block_size=16), 100, mqa.MQA_ERR_UNSUPPORTED),   # the page's block sizes 16/64/256
-    (dict(block_size=64), 100, mqa.MQA_ERR_UNSUPPORTED),
-    (dict(block_size=256), 100, mqa.MQA_ERR_UNSUPPORTED),
+    (dict(block_size=0), 100, mqa.MQA_ERR_SHAPE),
+    (dict(block_size=3), 100, mqa.MQA_ERR_UNSUPPORTED),    # not a power of two
+    (dict(block_size=48), 100, mqa.MQA_ERR_UNSUPPORTED),
+    (dict(block_size=1 << 17), 100, mqa.MQA_ERR_UNSUPPORTED),
+    (dict(block_size=64, block_table_stride=1 << 25), 100, mqa.MQA_ERR_UNSUPPORTED),  # W*S >= 2^31
+    (dict(block_size=64, num_blocks=1 << 25), 100, mqa.MQA_ERR_UNSUPPORTED),          # rows >= 2^31
     (dict(heads=24), 100, mqa.MQA_ERR_UNSUPPORTED),
     (dict(heads=144), 100, mqa.MQA_ERR_UNSUPPORTED),
     (dict(next_n=5), 100, mqa.MQA_ERR_UNSUPPORTED),
@@ -123,5 +126,5 @@ def test_empty_batch_is_a_no_op():
 
 def test_workspace_size_query():
     assert mqa.mqa_topk_workspace_bytes(good_shape(), 100, 2048) >= 0
-    assert mqa.mqa_topk_workspace_bytes(good_shape(block_size=2), 100, 2048) == 0
+    assert mqa.mqa_topk_workspace_bytes(good_shape(block_size=3), 100, 2048) == 0
     assert mqa.mqa_topk_workspace_bytes(good_shape(), 100, 0) == 0

@@ -193,3 +193,22 @@ def test_graph_replay_matches_eager():
         assert torch.equal(torch.sort(idx, dim=1).values, ref_idx), rep
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("block_size", [16, 64])
+def test_block_size_identity_bitwise(block_size):
+    """A cache in blocks of S (permuted blocks) gives bit-identical logits and the same
+    selections as a block_size 1 cache holding each token's row behind a per-token table."""
+    case = wl.make_case(batch=4, next_n=2, heads=64, ctx=[5, 1000, 2049, 4097], max_model_len=4100,
+                        seed=61 + block_size, block_size=block_size, pool=600)
+    gS, iS = run_gpu(case)
+    rows = case.kv_cache.reshape(-1, 132)
+    bt1 = np.full((case.batch, 4100), -1, dtype=np.int32)
+    for b in range(case.batch):
+        t = np.arange(int(case.context_lens[b]))
+        bt1[b, :t.size] = case.block_tables[b, t // block_size] * block_size + t % block_size
+    case1 = wl.Workload("per-token", case.q, rows, case.weights, case.context_lens, bt1,
+                        case.max_model_len, case.next_n)
+    g1, i1 = run_gpu(case1)
+    assert np.array_equal(gS.view(np.uint32), g1.view(np.uint32))
+    assert np.array_equal(np.sort(iS, axis=1), np.sort(i1, axis=1))

@@ -113,3 +113,19 @@ def test_k_values(k):
     case = wl.make_case(batch=6, next_n=2, heads=32, ctx=[1, 2, 100, 2048, 2050, 9000],
                         max_model_len=9000, seed=4000 + k, k=k)
     _parity(case, k=k, what=f"k={k}")
+
+
+# block_size > 1: token t is slot t % S of block table[t // S] (the page's reference walks
+# blocks; the page lists 16, 64 and 256 as the block sizes tried). Context lengths that
+# end mid-block, a permuted block pool and one interleaved across requests.
+@pytest.mark.parametrize("block_size,table", [(2, "permuted"), (16, "permuted"), (64, "interleaved"),
+                                              (256, "permuted")])
+@pytest.mark.parametrize("next_n,heads", [(1, 64), (2, 32), (4, 32)])
+def test_block_sizes(block_size, table, next_n, heads):
+    ctx = [1, 15, 16, 17, 63, 64, 65, 255, 257, 2049, 4100]
+    nblk = sum((c + block_size - 1) // block_size for c in ctx)
+    case = wl.make_case(batch=len(ctx), next_n=next_n, heads=heads, ctx=ctx, max_model_len=4160,
+                        seed=5000 + block_size + 10 * next_n, table=table, block_size=block_size,
+                        pool=nblk + 7)
+    assert case.block_size == block_size
+    _parity(case, what=f"S={block_size} {table} N={next_n} H={heads}")

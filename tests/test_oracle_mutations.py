@@ -27,8 +27,11 @@ MUTANTS = [
     ("causal window one long", "ctx - next_n + j + 1, max_model_len", "ctx - next_n + j + 2, max_model_len"),
     ("next_n offset ignored", "ctx - next_n + j + 1, max_model_len", "ctx, max_model_len"),
     ("weights of row b*N", "@ w[b * N + j]", "@ w[b * N]"),
-    ("block table ignored", "phys = block_tables[b, :ctx].astype(np.int64)",
+    ("block table ignored", "phys = token_rows(block_tables[b], ctx, bs)",
      "phys = np.arange(ctx, dtype=np.int64)"),
+    ("block slot ignored", "* block_size + t % block_size", "* block_size"),
+    ("block index by token", "np.asarray(table_row)[t // block_size]", "np.asarray(table_row)[t]"),
+    ("block size ignored", "return 1 if kv.ndim == 2 else int(kv.shape[1])", "return 1"),
     ("query of decode row 0 for every row", "score = k_b[:nv] @ qv[b, j].T", "score = k_b[:nv] @ qv[b, 0].T"),
     ("query head/dim transposed", "score = k_b[:nv] @ qv[b, j].T",
      "score = k_b[:nv, :qv.shape[2]] @ qv[b, j][:, :qv.shape[2]]"),
