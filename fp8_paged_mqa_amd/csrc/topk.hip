@@ -439,11 +439,36 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
   }
 }
 
-// Schedule for long-row mode (one workgroup): classifies every row, lists the rows of
-// each class and the long rows' chunks (offsets from block scans), and clears the long
-// rows' histograms and counters.
+// This workgroup's share of the histograms of `nlong` long-row slots (8-byte stores:
+// the workspace is 8-byte aligned).
+__device__ void clear_long_hist(const Params& p, uint32_t nlong) {
+  uint2* gh = reinterpret_cast<uint2*>(p.hist);
+  const int64_t words = (int64_t)nlong * (kKeyBins / 2);
+  const int64_t per = (words + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < words ? lo + per : words;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) gh[i] = make_uint2(0u, 0u);
+}
+
+// Schedule for long-row mode. Workgroup 0 classifies every row, lists the rows of each
+// class and the long rows' chunks (offsets from block scans) and clears the long rows'
+// counters; every workgroup counts the long rows and clears its share of their
+// histograms (16 KB each: one workgroup alone spent tens of microseconds on it).
 __global__ __launch_bounds__(kThreads) void topk_schedule_kernel(Params p) {
   __shared__ Core sh;
+  if (blockIdx.x != 0) {
+    uint32_t nlong = 0;
+    for (int base = 0; base < p.rows; base += kThreads) {
+      const int r = base + (int)threadIdx.x;
+      const int nv = r < p.rows ? visible(p, r) : 0;
+      uint32_t tl;
+      block_exclusive_scan((r < p.rows && nv > p.k && nv > kChunk) ? 1u : 0u, sh, kRedLo, tl);
+      nlong += tl;
+      __syncthreads();  // the scratch slots are reused by the next block of rows
+    }
+    clear_long_hist(p, nlong);
+    return;
+  }
   uint32_t off_l = 0, off_s = 0, off_t = 0, off_c = 0;
   for (int base = 0; base < p.rows; base += kThreads) {
     const int r = base + (int)threadIdx.x;
@@ -476,9 +501,7 @@ __global__ __launch_bounds__(kThreads) void topk_schedule_kernel(Params p) {
     off_c += tc;
     __syncthreads();  // the scratch slots are reused by the next block of rows
   }
-  uint2* gh = reinterpret_cast<uint2*>(p.hist);
-  const int64_t words2 = (int64_t)off_l * (kKeyBins / 2);
-  for (int64_t i = threadIdx.x; i < words2; i += kThreads) gh[i] = make_uint2(0u, 0u);
+  clear_long_hist(p, off_l);
   if (threadIdx.x == 0) {
     p.meta[kMetaLong] = off_l;
     p.meta[kMetaChunks] = off_c;
@@ -642,7 +665,7 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
   p.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
   p.cand = reinterpret_cast<uint64_t*>(ws + l.cand);
   const unsigned persistent = (unsigned)compute_units();
-  hipLaunchKernelGGL(topk_schedule_kernel, dim3(1), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(topk_schedule_kernel, dim3(persistent), dim3(kThreads), 0, stream, p);
   hipLaunchKernelGGL(topk_rows_kernel, dim3(persistent), dim3(kThreads), 0, stream, p);
   hipLaunchKernelGGL(topk_split_kernel, dim3(persistent), dim3(kThreads), 0, stream, p);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(persistent), dim3(kThreads), 0, stream, p);
