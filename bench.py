@@ -1,6 +1,7 @@
 """Throughput of the fp8 paged MQA indexer (logits + top-2048) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 1..5] [--block-size S] [--no-cpu-baseline]
+    python bench.py --op kwrite [--tokens T]   (the K-cache write alone; not the default line)
 
 One step = mqa_paged_logits + mqa_topk over one batch of the named synthetic workload,
 inputs already resident in HBM. Steps are captured into a HIP graph and replayed (the
@@ -95,6 +96,53 @@ def cpu_baseline(w, min_seconds=10.0):
             "sample": f"the whole workload (logits + top-{w.k}, float64 numpy), {runs} run(s) in {el:.1f} s"}
 
 
+def bench_kwrite(args):
+    """Tokens/s of mqa_indexer_k_write: T bf16 key rows quantised into a 600k-row cache at
+    permuted slots (8 rotating copies, graph replays)."""
+    import torch
+    sys.path.insert(0, ROOT)
+    from fp8_paged_mqa_amd import mqa
+    T, nslots, C = args.tokens, 600_000, max(1, args.copies)
+    rng = np.random.Generator(np.random.PCG64(7))
+    copies = []
+    for _ in range(C):
+        k = torch.from_numpy((rng.standard_normal((T, 128), dtype=np.float32)
+                              * rng.lognormal(0, 1, size=(T, 1)).astype(np.float32))).to(torch.bfloat16).cuda()
+        slots = torch.from_numpy(rng.permutation(nslots)[:T].astype(np.int64)).cuda()
+        kv = torch.zeros((nslots, 132), dtype=torch.uint8, device="cuda")
+        copies.append((k, slots, kv))
+    def run(c):
+        mqa.mqa_indexer_k_write(*c)
+    for i in range(4):
+        run(copies[i % C])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(C):
+            run(copies[i])
+    for _ in range(max(1, args.warmup // C)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // C)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * C)
+    nbytes = T * (256 + 8 + 132)  # bf16 keys + slot read, row written
+    achieved = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "indexer K-cache write tokens/s (bf16 keys -> e4m3fn + fp32 scale rows)",
+        "value": T / (us * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": reps * C, "warmup": args.warmup,
+        "us_per_call": us, "higher_is_better": True, "dtype": "bf16->fp8e4m3fn", "data": "synthetic",
+        "config": {"workload": f"{T} tokens into a {nslots}-row cache at permuted slots", "tokens": T},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "kernel": "k_write_kernel<true>",
+                     "algorithmic_bytes": nbytes, "traffic": None}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +153,8 @@ def main():
     ap.add_argument("--block-size", type=int, default=1,
                     help="tokens per KV block (1: the pages' layout; the default line uses 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="step", choices=["step", "kwrite"])
+    ap.add_argument("--tokens", type=int, default=65536, help="tokens per call for --op kwrite")
     ap.add_argument("--calibrate-copy-mib", type=int, default=256,
                     help="size of the plain device copy run once for counter calibration (0: skip)")
     args = ap.parse_args()
@@ -112,6 +162,9 @@ def main():
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
+    if args.op == "kwrite":
+        bench_kwrite(args)
+        return
 
     import torch
     sys.path.insert(0, ROOT)

@@ -121,4 +121,23 @@ int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model
   return mqa::launch_topk(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
+int mqa_indexer_k_write(const void* k, int32_t k_dtype, int64_t num_tokens, const int64_t* slot_mapping,
+                        uint8_t* kv_cache, int64_t num_slots, hipStream_t stream) {
+  if (num_tokens < 0 || num_slots < 1) return MQA_ERR_SHAPE;
+  if (k_dtype != MQA_DTYPE_BF16 && k_dtype != MQA_DTYPE_F32) return MQA_ERR_UNSUPPORTED;
+  if (num_slots > INT64_MAX / 132) return MQA_ERR_SHAPE;
+  if (num_tokens == 0) return MQA_OK;
+  if (!k || !slot_mapping || !kv_cache) return MQA_ERR_NULL;
+  if (!aligned(k, 16) || !aligned(slot_mapping, 8) || !aligned(kv_cache, 4))
+    return MQA_ERR_UNSUPPORTED;
+  mqa::KWriteLaunch a;
+  a.k = k;
+  a.slots = slot_mapping;
+  a.kv = kv_cache;
+  a.num_tokens = num_tokens;
+  a.num_slots = num_slots;
+  a.bf16 = k_dtype == MQA_DTYPE_BF16;
+  return mqa::launch_k_write(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
 }  // extern "C"

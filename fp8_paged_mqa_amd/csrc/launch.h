@@ -30,6 +30,17 @@ struct TopkLaunch {
   int32_t token_capacity;  // block_table_stride * block_size: tokens a table row can address
 };
 
+struct KWriteLaunch {
+  const void* k;          // [num_tokens, 128] bf16 or fp32
+  const int64_t* slots;   // [num_tokens] cache row of each token (outside [0, num_slots): skipped)
+  uint8_t* kv;            // [num_slots, 132]
+  int64_t num_tokens, num_slots;
+  bool bf16;
+};
+
+// Enqueue the K-cache write on `stream`.
+hipError_t launch_k_write(const KWriteLaunch& a, hipStream_t stream);
+
 // Device scratch the top-k launch needs for `rows` rows of length max_model_len
 // (0 when every row fits one workgroup).
 size_t topk_workspace_bytes(int64_t rows, int32_t max_model_len);

@@ -17,7 +17,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa.so")
 
 MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED, MQA_ERR_WORKSPACE, MQA_ERR_HIP = range(6)
 
-EXPORTS = ("mqa_paged_logits", "mqa_topk", "mqa_topk_workspace_bytes", "mqa_status_string")
+EXPORTS = ("mqa_paged_logits", "mqa_topk", "mqa_topk_workspace_bytes", "mqa_status_string",
+           "mqa_indexer_k_write")
+MQA_DTYPE_BF16, MQA_DTYPE_F32 = 0, 1
 
 
 class mqa_shape(ctypes.Structure):
@@ -46,6 +48,9 @@ def _load() -> ctypes.CDLL:
     lib.mqa_topk_workspace_bytes.restype = sz
     lib.mqa_status_string.argtypes = [ctypes.c_int]
     lib.mqa_status_string.restype = ctypes.c_char_p
+    i64 = ctypes.c_int64
+    lib.mqa_indexer_k_write.argtypes = [vp, i32, i64, vp, vp, i64, vp]
+    lib.mqa_indexer_k_write.restype = ctypes.c_int
     return lib
 
 
@@ -107,6 +112,23 @@ def mqa_topk(logits, context_lens, max_model_len, k, idx, shape: mqa_shape, work
                        ctypes.byref(shape), _ptr(workspace), ws_bytes, _stream(stream))
     if check and st != MQA_OK:
         raise MqaError(st, "mqa_topk")
+    return st
+
+
+def mqa_indexer_k_write(k, slot_mapping, kv_cache, stream=None, check: bool = True) -> int:
+    """Quantise k [T, 128] (bf16 or fp32) into the cache rows slot_mapping (int64 [T])
+    of kv_cache (uint8 [num_slots, 132] or [num_blocks, block_size, (1,) 132])."""
+    if k.dtype == torch.bfloat16:
+        dtype = MQA_DTYPE_BF16
+    elif k.dtype == torch.float32:
+        dtype = MQA_DTYPE_F32
+    else:
+        dtype = -1  # rejected by the library
+    num_slots = kv_cache.numel() // 132
+    st = _lib.mqa_indexer_k_write(_ptr(k), dtype, int(k.shape[0]), _ptr(slot_mapping), _ptr(kv_cache),
+                                  int(num_slots), _stream(stream))
+    if check and st != MQA_OK:
+        raise MqaError(st, "mqa_indexer_k_write")
     return st
 
 

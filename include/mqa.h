@@ -134,6 +134,39 @@ int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model
              int32_t k, int32_t* idx, const mqa_shape* shape, void* workspace,
              size_t workspace_bytes, hipStream_t stream);
 
+/* Element types of the keys given to mqa_indexer_k_write. */
+enum { MQA_DTYPE_BF16 = 0, MQA_DTYPE_F32 = 1 };
+
+/*
+ * mqa_indexer_k_write - quantise keys into the cache rows mqa_paged_logits reads.
+ *
+ * Row format (stepcodex.com pa_mqa_logits issue, "Minimal reproduction": the reference
+ * reads bytes [0, 128) of a token's row as e4m3fn codes and bytes [128, 132) as one
+ * little-endian fp32 scale, and dequantises code * scale). The page does not state how
+ * a writer picks the scale; this call maps the row's largest magnitude onto the largest
+ * finite code:
+ *     amax  = max_i |k[t, i]|
+ *     scale = amax / 448 in fp32, correctly rounded (scale = 1 when amax = 0)
+ *     code  = e4m3fn(k[t, i] / scale): the fp32 quotient, correctly rounded, then the
+ *             nearest e4m3fn value, ties to even (so |code| <= 448; a NaN key makes
+ *             the row NaN, an infinite key gives an infinite scale)
+ * and writes row slot_mapping[t] (row blk * block_size + offset of a blocked cache):
+ *     kv_cache[slot*132 + 0 .. 127] = codes, kv_cache[slot*132 + 128 .. 131] = scale.
+ * Tokens whose slot lies outside [0, num_slots) are skipped (negative slots mark
+ * padding). Two tokens mapped to one slot race; the result is one of them.
+ *
+ *   k             [num_tokens, 128] contiguous, bf16 (MQA_DTYPE_BF16) or fp32
+ *                 (MQA_DTYPE_F32), 16-byte aligned
+ *   k_dtype       MQA_DTYPE_BF16 or MQA_DTYPE_F32
+ *   num_tokens    T >= 0 (0 enqueues nothing)
+ *   slot_mapping  int64 [T], 8-byte aligned
+ *   kv_cache      uint8 [num_slots, 132], 4-byte aligned
+ *   num_slots     rows of the cache (num_blocks * block_size), >= 1
+ * Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED or MQA_ERR_HIP.
+ */
+int mqa_indexer_k_write(const void* k, int32_t k_dtype, int64_t num_tokens, const int64_t* slot_mapping,
+                        uint8_t* kv_cache, int64_t num_slots, hipStream_t stream);
+
 /* Workspace size for mqa_topk with this shape, L and k (0 when the shape is invalid). */
 size_t mqa_topk_workspace_bytes(const mqa_shape* shape, int32_t max_model_len, int32_t k);
 

@@ -210,3 +210,70 @@ def topk(logits, context_lens, next_n, k, max_model_len=None):
         sel = topk_row(logits[r, :nv], k)
         out[r, :sel.size] = sel
     return out
+
+
+# ---------------------------------------------------------------------------
+# Upstream of the op: writing the indexer's keys into the cache.
+#
+# The page's reference reads a token's row as 128 e4m3fn codes times one fp32
+# scale (bytes [D, D+4) of the row). The page does not say how the writer picks
+# that scale; the reading taken here is the per-token absolute maximum mapped
+# onto the largest finite e4m3fn value: scale = amax / 448 in fp32, codes =
+# e4m3fn(x / scale) with x / scale computed in fp32 and rounded to nearest even.
+# A row of zeros gets scale 1 and zero codes. NaN inputs give NaN codes and
+# scale; an input of infinite magnitude gives an infinite scale.
+# ---------------------------------------------------------------------------
+E4M3FN_MAX = 448.0
+
+
+def encode_e4m3fn(x) -> np.ndarray:
+    """Round each float64 value to the nearest e4m3fn code, ties to the even code
+    (OCP FP8 E4M3 with the fn convention: no infinities, S.1111.111 is NaN).
+    Magnitudes that round above 448 become NaN, as in a non-saturating
+    conversion: 464, halfway between 448 and the next step 480, ties to 448
+    (even mantissa); anything larger overflows. Returns uint8 codes."""
+    x = np.asarray(x, dtype=np.float64)
+    finite_codes = np.arange(0x7F, dtype=np.uint8)          # 0x00 .. 0x7E: +0 .. 448
+    mags = E4M3FN_VALUES[finite_codes]                      # increasing
+    ax = np.abs(x)
+    hi = np.searchsorted(mags, ax, side="left")             # first code with value >= |x|
+    hi_c = np.minimum(hi, 0x7E)
+    lo_c = np.maximum(hi_c - 1, 0)
+    d_lo = ax - mags[lo_c]
+    d_hi = mags[hi_c] - ax
+    exact = mags[hi_c] == ax
+    take_hi = exact | (d_hi < d_lo) | ((d_hi == d_lo) & (hi_c % 2 == 0))
+    code = np.where(take_hi, hi_c, lo_c).astype(np.uint8)
+    # beyond 448: above the tie at 464 the value rounds to 480, which has no code
+    code = np.where(ax > 464.0, np.uint8(0x7F), code)
+    code = np.where(np.isnan(x), np.uint8(0x7F), code)
+    sign = (np.signbit(x) & ~np.isnan(x)).astype(np.uint8) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_k_row(k_row) -> tuple[np.ndarray, np.float32]:
+    """One token's 128 keys (float32 values) -> (128 e4m3fn codes, fp32 scale)."""
+    k32 = np.asarray(k_row, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(k32))) if not np.isnan(k32).any() else np.float32(np.nan)
+    if amax == 0:
+        return np.zeros(k32.shape, dtype=np.uint8), np.float32(1.0)
+    scale = np.float32(amax / np.float32(E4M3FN_MAX))       # fp32 division
+    scaled = (k32 / scale).astype(np.float32)                # fp32 division per element
+    return encode_e4m3fn(scaled.astype(np.float64)), scale
+
+
+def write_k_cache(k, slot_mapping, kv_cache):
+    """Returns a copy of ``kv_cache`` (uint8, [num_slots, D+4] or [num_blocks,
+    block_size, (1,) D+4]) with token i's row written at slot slot_mapping[i]
+    (row blk * block_size + offset); slots outside [0, num_slots) are skipped.
+    k is [T, D] float values (bf16 inputs are passed as their float32 values)."""
+    out = np.array(kv_cache, dtype=np.uint8, copy=True)
+    rows = out.reshape(-1, ROW_BYTES)
+    k = np.asarray(k, dtype=np.float32)
+    for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0 or slot >= rows.shape[0]:
+            continue
+        codes, scale = quantize_k_row(k[i])
+        rows[slot, :HEAD_DIM] = codes
+        rows[slot, HEAD_DIM:ROW_BYTES] = np.frombuffer(np.float32(scale).astype("<f4").tobytes(), dtype=np.uint8)
+    return out

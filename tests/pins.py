@@ -332,6 +332,88 @@ def pin_topk_ctx_k_plus_one_drops_argmin(orc):
         assert dropped == [int(minima.max())], (trial, dropped)
 
 
+# ---------------------------------------------------------------------------
+# K-cache write (quantisation upstream of the op)
+# ---------------------------------------------------------------------------
+def _encode_probe_values():
+    rng = np.random.default_rng(5)
+    vals = TORCH_E4M3[np.isfinite(TORCH_E4M3)]
+    mids = (np.sort(vals)[1:] + np.sort(vals)[:-1]) / 2
+    return np.concatenate([rng.standard_normal(20000) * 40, np.linspace(-470, 470, 9401), vals, mids,
+                           [0.0, -0.0, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11, 1e-30, 463.99, 464.0, 464.01,
+                            np.nan, np.inf, -np.inf]]).astype(np.float32)
+
+
+def pin_encode_matches_torch(orc):
+    """Round to nearest even e4m3fn, checked against torch's independent cast on random
+    values, a fine grid over the whole range, every code value, every midpoint between
+    neighbouring codes, the top-of-range tie at 464, and NaN / inf."""
+    x = _encode_probe_values()
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = orc.encode_e4m3fn(x.astype(np.float64))
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, (bad.size, x[bad][:5], got[bad][:5], ref[bad][:5])
+
+
+def pin_quantize_round_trip(orc):
+    """Dequantising a written row the way the page's reference reads the cache (code
+    value times the row's fp32 scale) returns each key to within half an e4m3 step,
+    and the row's largest magnitude lands exactly on +-448."""
+    rng = np.random.default_rng(6)
+    for trial in range(40):
+        k = (rng.standard_normal(128) * rng.lognormal(0, 3)).astype(np.float32)
+        if trial % 7 == 0:
+            k[rng.integers(0, 128, 5)] = 0.0
+        codes, scale = orc.quantize_k_row(k)
+        assert np.float32(scale) == np.float32(np.abs(k).max() / np.float32(448.0))
+        deq = TORCH_E4M3[codes] * float(scale)
+        y = k.astype(np.float64) / float(scale)                  # position on the e4m3 grid
+        # half a step: 2^-4 relative in the normal range, 2^-10 absolute (times scale) below 2^-6
+        bound = np.where(np.abs(y) >= 2.0 ** -6, np.abs(k) * 2.0 ** -4, 2.0 ** -10 * float(scale)) * (1 + 1e-6)
+        assert np.all(np.abs(deq - k) <= bound + 1e-30), trial
+        i = int(np.argmax(np.abs(k)))
+        assert TORCH_E4M3[codes[i]] == (448.0 if k[i] > 0 else -448.0)
+    codes, scale = orc.quantize_k_row(np.zeros(128, np.float32))
+    assert np.all(codes == 0) and scale == np.float32(1.0)
+
+
+def pin_write_slots_and_logits(orc):
+    """write_k_cache puts token i at slot_mapping[i] (row blk * S + offset for a blocked
+    cache), skips slots outside the cache, leaves every other byte alone; the logits of
+    the written cache equal a float64 evaluation on the dequantised keys."""
+    rng = np.random.default_rng(7)
+    T, S, nblk = 10, 4, 6
+    k = (rng.standard_normal((T, 128)) * 3).astype(np.float32)
+    cache = rng.integers(0, 256, size=(nblk, S, 132), dtype=np.uint8)
+    slots = np.array([5, 0, 23, -1, 9, 24, 11, 2, 17, 8])     # -1 and 24 lie outside
+    out = orc.write_k_cache(k, slots, cache)
+    rows_in, rows_out = cache.reshape(-1, 132), out.reshape(-1, 132)
+    written = {int(s_): i for i, s_ in enumerate(slots) if 0 <= s_ < nblk * S}
+    for r in range(nblk * S):
+        if r not in written:
+            assert np.array_equal(rows_out[r], rows_in[r]), r
+            continue
+        kk = k[written[r]]
+        scale = struct.unpack("<f", rows_out[r, 128:132].tobytes())[0]
+        assert scale == float(np.float32(np.abs(kk).max() / np.float32(448.0)))
+        ref_codes = torch.from_numpy((kk / np.float32(scale)).astype(np.float32)).to(torch.float8_e4m3fn)
+        assert np.array_equal(rows_out[r, :128], ref_codes.view(torch.uint8).numpy()), r
+    # logits over the written rows: request 0 reads tokens 0, 1, 2 (slots 5, 0, 23)
+    q = rng.integers(0, 256, size=(1, 1, 16, 128), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x38                                # no NaN query codes
+    w = rng.standard_normal((1, 16)).astype(np.float32)
+    bt = np.array([[1, 0, 5]])                                  # blocks: slot 5 = blk 1 off 1, ...
+    # tokens t=0..2 -> rows bt[t//4]*4 + t%4 = 4, 5, 6; write those slots with tokens 0..2
+    out2 = orc.write_k_cache(k[:3], np.array([4, 5, 6]), cache)
+    got = orc.paged_mqa_logits(q, out2, w, np.array([3]), bt, 3)
+    for t in range(3):
+        row = out2.reshape(-1, 132)[4 + t]
+        scale = struct.unpack("<f", row[128:132].tobytes())[0]
+        key = TORCH_E4M3[row[:128]] * scale
+        want = sum(float(w[0, h]) * max(float(np.dot(TORCH_E4M3[q[0, 0, h]], key)), 0.0) for h in range(16))
+        assert abs(got[0, t] - want) <= 1e-9 * (1 + abs(want)), (t, got[0, t], want)
+
+
 PINS = [
     pin_block_size_identity,
     pin_decode_matches_torch,
@@ -347,4 +429,7 @@ PINS = [
     pin_topk_counting_definition,
     pin_topk_rows_and_padding,
     pin_topk_ctx_k_plus_one_drops_argmin,
+    pin_encode_matches_torch,
+    pin_quantize_round_trip,
+    pin_write_slots_and_logits,
 ]

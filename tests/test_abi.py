@@ -128,3 +128,29 @@ def test_workspace_size_query():
     assert mqa.mqa_topk_workspace_bytes(good_shape(), 100, 2048) >= 0
     assert mqa.mqa_topk_workspace_bytes(good_shape(block_size=3), 100, 2048) == 0
     assert mqa.mqa_topk_workspace_bytes(good_shape(), 100, 0) == 0
+
+
+def call_kwrite(dtype=0, T=4, nslots=100, ptrs=(FAKE,) * 3):
+    k, slots, kv = ptrs
+    return mqa._lib.mqa_indexer_k_write(k, dtype, T, slots, kv, nslots, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), mqa.MQA_ERR_SHAPE),
+    (dict(nslots=0), mqa.MQA_ERR_SHAPE),
+    (dict(dtype=2), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(dtype=-1), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(ptrs=(None, FAKE, FAKE)), mqa.MQA_ERR_NULL),
+    (dict(ptrs=(FAKE, None, FAKE)), mqa.MQA_ERR_NULL),
+    (dict(ptrs=(FAKE, FAKE, None)), mqa.MQA_ERR_NULL),
+    (dict(ptrs=(ctypes.c_void_p(0x10008), FAKE, FAKE)), mqa.MQA_ERR_UNSUPPORTED),      # keys need 16 B
+    (dict(dtype=1, ptrs=(ctypes.c_void_p(0x10004), FAKE, FAKE)), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(ptrs=(FAKE, ctypes.c_void_p(0x10004), FAKE)), mqa.MQA_ERR_UNSUPPORTED),      # int64 slots need 8 B
+    (dict(ptrs=(FAKE, FAKE, ctypes.c_void_p(0x10002))), mqa.MQA_ERR_UNSUPPORTED),
+])
+def test_k_write_rejects(kw, status):
+    assert call_kwrite(**kw) == status
+
+
+def test_k_write_zero_tokens_is_a_no_op():
+    assert call_kwrite(T=0, ptrs=(None,) * 3) == mqa.MQA_OK

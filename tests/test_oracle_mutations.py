@@ -39,6 +39,12 @@ MUTANTS = [
      "order = np.lexsort((np.arange(values.size), values))"),
     ("top-k ties to highest position", "order = np.lexsort((np.arange(values.size), -values))",
      "order = np.lexsort((-np.arange(values.size), -values))"),
+    ("encode ties away from zero", "((d_hi == d_lo) & (hi_c % 2 == 0))", "(d_hi == d_lo)"),
+    ("encode truncates", "take_hi = exact | (d_hi < d_lo) | ((d_hi == d_lo) & (hi_c % 2 == 0))", "take_hi = exact"),
+    ("encode saturates", "code = np.where(ax > 464.0, np.uint8(0x7F), code)", "code = code"),
+    ("scale maps amax to 240", "scale = np.float32(amax / np.float32(E4M3FN_MAX))", "scale = np.float32(amax / np.float32(240.0))"),
+    ("scale multiplies", "scaled = (k32 / scale).astype(np.float32)", "scaled = (k32 * scale).astype(np.float32)"),
+    ("write ignores the slot", "rows[slot, :HEAD_DIM] = codes", "rows[i, :HEAD_DIM] = codes"),
     ("top-k one short", "return np.sort(order[:min(k, values.size)])",
      "return np.sort(order[:min(k, values.size) - 1])"),
 ]
