@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--config 1..5] [--block-size S] [--no-cpu-baseline]
     python bench.py --op kwrite [--tokens T]   (the K-cache write alone; not the default line)
+    python bench.py --op prefill [--m M --n N --heads H]   (non-paged logits; not the default line)
 
 One step = mqa_paged_logits + mqa_topk over one batch of the named synthetic workload,
 inputs already resident in HBM. Steps are captured into a HIP graph and replayed (the
@@ -96,6 +97,61 @@ def cpu_baseline(w, min_seconds=10.0):
             "sample": f"the whole workload (logits + top-{w.k}, float64 numpy), {runs} run(s) in {el:.1f} s"}
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(args):
+    """Non-paged logits: M query rows (causal: row i sees keys [0, N - M + i]) over N keys,
+    8 rotating input/output copies, graph replays. Bound by the f16 matrix cores it uses."""
+    import torch
+    sys.path.insert(0, ROOT)
+    from fp8_paged_mqa_amd import mqa, workloads
+    M, N, H, C = args.m, args.n, args.heads, max(1, min(args.copies, 4))
+    rng = np.random.Generator(np.random.PCG64(11))
+    ks = np.zeros(M, np.int32)
+    ke = (np.arange(M) + (N - M) + 1).astype(np.int32)
+    copies = []
+    for _ in range(C):
+        q = torch.from_numpy(workloads.to_e4m3fn_bytes(rng.standard_normal((M, H, 128), dtype=np.float32))).cuda()
+        k = torch.from_numpy(workloads.to_e4m3fn_bytes(rng.standard_normal((N, 128), dtype=np.float32))).cuda()
+        sc = torch.from_numpy(rng.lognormal(0, 0.5, size=N).astype(np.float32)).cuda()
+        w = torch.from_numpy(rng.standard_normal((M, H), dtype=np.float32)).cuda()
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        copies.append((q, k, sc, w, torch.from_numpy(ks).cuda(), torch.from_numpy(ke).cuda(), out))
+    def run(c):
+        mqa.mqa_logits(*c)
+    for i in range(3):
+        run(copies[i % C])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(C):
+            run(copies[i])
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // (4 * C))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * C)
+    visible = int(np.clip(ke - ks, 0, N).astype(np.int64).sum())
+    flops = 2.0 * H * 128 * visible
+    nbytes = M * H * 128 + N * 132 + 4 * M * H + 8 * M + 4 * M * N
+    tflops = flops / (us * 1e-6) / 1e12
+    print(json.dumps({
+        "metric": "non-paged (prefill) indexer logits, TFLOP/s of the contraction",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": reps * C, "us_per_call": us,
+        "higher_is_better": True, "dtype": "fp8e4m3fn->f16 mfma, f32 accumulate", "data": "synthetic",
+        "config": {"workload": f"M={M} query rows, N={N} keys, H={H}, causal windows", "m": M, "n": N, "heads": H},
+        "hbm_gbps_algorithmic": nbytes / (us * 1e-6) / 1e9,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_F16_PEAK_TFLOPS, "kernel": "prefill_logits_kernel",
+                     "algorithmic_flops": flops, "traffic": None}}), flush=True)
+
+
 def bench_kwrite(args):
     """Tokens/s of mqa_indexer_k_write: T bf16 key rows quantised into a 600k-row cache at
     permuted slots (8 rotating copies, graph replays)."""
@@ -153,7 +209,10 @@ def main():
     ap.add_argument("--block-size", type=int, default=1,
                     help="tokens per KV block (1: the pages' layout; the default line uses 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="step", choices=["step", "kwrite"])
+    ap.add_argument("--op", default="step", choices=["step", "kwrite", "prefill"])
+    ap.add_argument("--m", type=int, default=4096, help="query rows for --op prefill")
+    ap.add_argument("--n", type=int, default=8192, help="keys for --op prefill")
+    ap.add_argument("--heads", type=int, default=32, help="heads for --op prefill")
     ap.add_argument("--tokens", type=int, default=65536, help="tokens per call for --op kwrite")
     ap.add_argument("--calibrate-copy-mib", type=int, default=256,
                     help="size of the plain device copy run once for counter calibration (0: skip)")
@@ -164,6 +223,9 @@ def main():
         sys.exit(2)
     if args.op == "kwrite":
         bench_kwrite(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
         return
 
     import torch

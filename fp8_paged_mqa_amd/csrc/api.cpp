@@ -121,6 +121,31 @@ int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model
   return mqa::launch_topk(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
+int mqa_logits(const uint8_t* q, const uint8_t* k, const float* k_scale, const float* weights,
+               const int32_t* ks, const int32_t* ke, float* out, int64_t out_stride, int32_t m, int32_t n,
+               int32_t heads, hipStream_t stream) {
+  if (m < 0 || n < 1 || heads < 1 || out_stride < n) return MQA_ERR_SHAPE;
+  if (heads % 16 != 0 || heads > 64) return MQA_ERR_UNSUPPORTED;
+  if (m == 0) return MQA_OK;
+  if (!q || !k || !k_scale || !weights || !ks || !ke || !out) return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(weights, 16) || !aligned(k_scale, 4) || !aligned(ks, 4) ||
+      !aligned(ke, 4) || !aligned(out, 4))
+    return MQA_ERR_UNSUPPORTED;
+  mqa::PrefillLaunch a;
+  a.q = q;
+  a.k = k;
+  a.k_scale = k_scale;
+  a.w = weights;
+  a.ks = ks;
+  a.ke = ke;
+  a.out = out;
+  a.out_stride = out_stride;
+  a.m = m;
+  a.n = n;
+  a.heads = heads;
+  return mqa::launch_prefill(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
 int mqa_indexer_k_write(const void* k, int32_t k_dtype, int64_t num_tokens, const int64_t* slot_mapping,
                         uint8_t* kv_cache, int64_t num_slots, hipStream_t stream) {
   if (num_tokens < 0 || num_slots < 1) return MQA_ERR_SHAPE;

@@ -30,6 +30,21 @@ struct TopkLaunch {
   int32_t token_capacity;  // block_table_stride * block_size: tokens a table row can address
 };
 
+struct PrefillLaunch {
+  const uint8_t* q;       // [m, heads, 128]
+  const uint8_t* k;       // [n, 128]
+  const float* k_scale;   // [n]
+  const float* w;         // [m, heads]
+  const int32_t* ks;      // [m]
+  const int32_t* ke;      // [m]
+  float* out;             // [m, out_stride]
+  int64_t out_stride;
+  int32_t m, n, heads;
+};
+
+// Enqueue the non-paged logits kernel on `stream`.
+hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+
 struct KWriteLaunch {
   const void* k;          // [num_tokens, 128] bf16 or fp32
   const int64_t* slots;   // [num_tokens] cache row of each token (outside [0, num_slots): skipped)

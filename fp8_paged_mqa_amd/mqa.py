@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa.so")
 MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED, MQA_ERR_WORKSPACE, MQA_ERR_HIP = range(6)
 
 EXPORTS = ("mqa_paged_logits", "mqa_topk", "mqa_topk_workspace_bytes", "mqa_status_string",
-           "mqa_indexer_k_write")
+           "mqa_indexer_k_write", "mqa_logits")
 MQA_DTYPE_BF16, MQA_DTYPE_F32 = 0, 1
 
 
@@ -51,6 +51,8 @@ def _load() -> ctypes.CDLL:
     i64 = ctypes.c_int64
     lib.mqa_indexer_k_write.argtypes = [vp, i32, i64, vp, vp, i64, vp]
     lib.mqa_indexer_k_write.restype = ctypes.c_int
+    lib.mqa_logits.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
+    lib.mqa_logits.restype = ctypes.c_int
     return lib
 
 
@@ -112,6 +114,18 @@ def mqa_topk(logits, context_lens, max_model_len, k, idx, shape: mqa_shape, work
                        ctypes.byref(shape), _ptr(workspace), ws_bytes, _stream(stream))
     if check and st != MQA_OK:
         raise MqaError(st, "mqa_topk")
+    return st
+
+
+def mqa_logits(q, k, k_scale, weights, ks, ke, out, stream=None, check: bool = True) -> int:
+    """out[M, >= N] <- non-paged logits: q uint8 [M,H,128], k uint8 [N,128], k_scale f32 [N],
+    weights f32 [M,H], ks/ke i32 [M] (row i sees keys [ks[i], ke[i]))."""
+    M, H, _ = q.shape
+    N = k.shape[0]
+    st = _lib.mqa_logits(_ptr(q), _ptr(k), _ptr(k_scale), _ptr(weights), _ptr(ks), _ptr(ke), _ptr(out),
+                         int(out.stride(0)), int(M), int(N), int(H), _stream(stream))
+    if check and st != MQA_OK:
+        raise MqaError(st, "mqa_logits")
     return st
 
 

@@ -134,6 +134,32 @@ int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model
              int32_t k, int32_t* idx, const mqa_shape* shape, void* workspace,
              size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * mqa_logits - the same logits over contiguous keys for M query rows with per-row key
+ * windows (the non-paged, prefill form).
+ *
+ * Definition: the quantity of mqa_paged_logits; the stepcodex.com pa_mqa_logits issue
+ * ("Observations while narrowing it down") names the prefill kernel that computes it for
+ * many query rows at once (fp8_mqa_logits) but not its signature. Here:
+ *     out[i*out_stride + j] = sum_h weights[i*H + h] * relu(k_scale[j] * (q[i,h,:] . k[j,:]))
+ *                             if ks[i] <= j < ke[i], and -inf for every other j < n,
+ * with ks[i], ke[i] read as clamped to [0, n] (an empty window leaves the row -inf).
+ *
+ *   q           uint8 [m, H, 128]  e4m3fn, 16-byte aligned
+ *   k           uint8 [n, 128]     e4m3fn, 16-byte aligned
+ *   k_scale     float [n]          per-key dequant scale
+ *   weights     float [m, H]       16-byte aligned
+ *   ks, ke      int32 [m]
+ *   out         float [m, out_stride], out_stride >= n; elements [n, out_stride) of a row
+ *               are not touched
+ *   m >= 0 (0 enqueues nothing), n >= 1, heads a multiple of 16 in [16, 64]
+ * Accuracy as mqa_paged_logits (exact fp8 products, fp32 accumulation).
+ * Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED or MQA_ERR_HIP.
+ */
+int mqa_logits(const uint8_t* q, const uint8_t* k, const float* k_scale, const float* weights,
+               const int32_t* ks, const int32_t* ke, float* out, int64_t out_stride, int32_t m, int32_t n,
+               int32_t heads, hipStream_t stream);
+
 /* Element types of the keys given to mqa_indexer_k_write. */
 enum { MQA_DTYPE_BF16 = 0, MQA_DTYPE_F32 = 1 };
 

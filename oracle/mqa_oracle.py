@@ -277,3 +277,41 @@ def write_k_cache(k, slot_mapping, kv_cache):
         rows[slot, :HEAD_DIM] = codes
         rows[slot, HEAD_DIM:ROW_BYTES] = np.frombuffer(np.float32(scale).astype("<f4").tobytes(), dtype=np.uint8)
     return out
+
+
+# ---------------------------------------------------------------------------
+# The non-paged (prefill) form of the same logits. The page names the prefill
+# indexer kernel (aiter's fp8_mqa_logits) in "Observations while narrowing it
+# down" as computing the same quantity over contiguous keys for M query rows, but
+# gives no signature. Reading taken: keys are contiguous (codes [N, D] plus one
+# fp32 scale per key), query row m sees keys n with ks[m] <= n < ke[m] (ranges
+# clamped to [0, N]; an empty range leaves the row -inf), and
+#   logit[m, n] = sum_h w[m, h] * relu(scale_n * (q[m, h, :] . k[n, :])).
+# ---------------------------------------------------------------------------
+def mqa_logits(q, k, k_scale, weights, ks, ke):
+    """Logits [M, N] float64.
+
+    q        uint8 [M, H, D]  e4m3fn bytes
+    k        uint8 [N, D]     e4m3fn bytes
+    k_scale  float [N]
+    weights  float [M, H]
+    ks, ke   int   [M]        query row m sees keys [ks[m], ke[m])
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    M, H, D = q.shape
+    assert D == HEAD_DIM
+    keys = decode_bytes(np.asarray(k, dtype=np.uint8))             # [N, D]
+    N = keys.shape[0]
+    scales = np.asarray(k_scale, dtype=np.float32).astype(np.float64)
+    w = np.asarray(weights, dtype=np.float64).reshape(M, H)
+    qv = decode_bytes(q)                                            # [M, H, D]
+    out = np.full((M, N), -np.inf, dtype=np.float64)
+    for m in range(M):
+        lo = min(max(int(ks[m]), 0), N)
+        hi = min(max(int(ke[m]), 0), N)
+        if hi <= lo:
+            continue
+        score = keys[lo:hi] @ qv[m].T                               # [n, H], exact
+        x = score * scales[lo:hi, None]
+        out[m, lo:hi] = np.maximum(x, 0.0) @ w[m]
+    return out

@@ -414,6 +414,60 @@ def pin_write_slots_and_logits(orc):
         assert abs(got[0, t] - want) <= 1e-9 * (1 + abs(want)), (t, got[0, t], want)
 
 
+# ---------------------------------------------------------------------------
+# Non-paged (prefill) logits
+# ---------------------------------------------------------------------------
+def _split_rows(kv):
+    rows = np.asarray(kv, dtype=np.uint8).reshape(-1, 132)
+    return rows[:, :128].copy(), np.ascontiguousarray(rows[:, 128:132]).view("<f4")[:, 0].copy()
+
+
+def pin_prefill_exact_rationals(orc):
+    """Fraction brute force of the prefill form on tiny shapes with arbitrary windows
+    (empty, clipped at both ends, reversed)."""
+    rng = np.random.default_rng(8)
+    for trial, (M, H, N) in enumerate([(3, 2, 6), (4, 1, 5), (2, 3, 7)]):
+        case = wl.make_case(batch=1, next_n=1, heads=H, ctx=[N], seed=300 + trial, table="identity")
+        k, sc = _split_rows(case.kv_cache[:N])
+        q = rng.integers(0, 256, size=(M, H, 128), dtype=np.uint8)
+        q[(q & 0x7F) == 0x7F] = 0x38
+        w = rng.standard_normal((M, H)).astype(np.float32)
+        ks = rng.integers(-2, N + 1, size=M)
+        ke = rng.integers(-1, N + 3, size=M)
+        ks[0], ke[0] = 0, N
+        got = orc.mqa_logits(q, k, sc, w, ks, ke)
+        for m in range(M):
+            for n in range(N):
+                if not (max(ks[m], 0) <= n < min(ke[m], N)):
+                    assert got[m, n] == -np.inf, (trial, m, n)
+                    continue
+                total, terms = Fraction(0), Fraction(0)
+                for h in range(H):
+                    dot = sum(Fraction(TORCH_E4M3[q[m, h, i]]) * Fraction(TORCH_E4M3[k[n, i]]) for i in range(128))
+                    x = dot * Fraction(float(sc[n]))
+                    term = Fraction(float(w[m, h])) * (x if x > 0 else Fraction(0))
+                    total += term
+                    terms += abs(term)
+                assert abs(got[m, n] - float(total)) <= 8 * H * 2.0 ** -53 * float(terms) + 1e-300, (trial, m, n)
+
+
+def pin_prefill_matches_decode_rows(orc):
+    """Decode rows are prefill rows over the request's keys: with ks = 0 and ke = the
+    row's visible count, the prefill form over the request's rows in logical order
+    reproduces the paged logits exactly (a separately pinned path)."""
+    case = wl.make_case(batch=2, next_n=3, heads=32, ctx=[40, 17], max_model_len=48, seed=301, table="permuted")
+    paged = orc.paged_mqa_logits(case.q, case.kv_cache, case.weights, case.context_lens, case.block_tables, 48)
+    for b in range(2):
+        ctx = int(case.context_lens[b])
+        k, sc = _split_rows(case.kv_cache[case.block_tables[b, :ctx]])
+        N = case.next_n
+        q = case.q[b]                                                # [N, H, D]
+        w = case.weights[b * N:(b + 1) * N]
+        ke = np.array([ctx - N + j + 1 for j in range(N)])
+        got = orc.mqa_logits(q, k, sc, w, np.zeros(N, int), ke)
+        assert np.array_equal(got, paged[b * N:(b + 1) * N, :ctx]), b
+
+
 PINS = [
     pin_block_size_identity,
     pin_decode_matches_torch,
@@ -432,4 +486,6 @@ PINS = [
     pin_encode_matches_torch,
     pin_quantize_round_trip,
     pin_write_slots_and_logits,
+    pin_prefill_exact_rationals,
+    pin_prefill_matches_decode_rows,
 ]

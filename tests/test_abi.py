@@ -154,3 +154,29 @@ def test_k_write_rejects(kw, status):
 
 def test_k_write_zero_tokens_is_a_no_op():
     assert call_kwrite(T=0, ptrs=(None,) * 3) == mqa.MQA_OK
+
+
+def call_prefill(m=4, n=64, heads=32, stride=64, ptrs=(FAKE,) * 7):
+    q, k, sc, w, ks, ke, out = ptrs
+    return mqa._lib.mqa_logits(q, k, sc, w, ks, ke, out, stride, m, n, heads, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=-1), mqa.MQA_ERR_SHAPE),
+    (dict(n=0), mqa.MQA_ERR_SHAPE),
+    (dict(heads=0), mqa.MQA_ERR_SHAPE),
+    (dict(stride=63), mqa.MQA_ERR_SHAPE),
+    (dict(heads=24), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(heads=80), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(ptrs=(None,) + (FAKE,) * 6), mqa.MQA_ERR_NULL),
+    (dict(ptrs=(FAKE,) * 6 + (None,)), mqa.MQA_ERR_NULL),
+    (dict(ptrs=(ctypes.c_void_p(0x10008),) + (FAKE,) * 6), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(ptrs=(FAKE, ctypes.c_void_p(0x10004)) + (FAKE,) * 5), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(ptrs=(FAKE,) * 3 + (ctypes.c_void_p(0x10004),) + (FAKE,) * 3), mqa.MQA_ERR_UNSUPPORTED),
+])
+def test_prefill_logits_rejects(kw, status):
+    assert call_prefill(**kw) == status
+
+
+def test_prefill_zero_rows_is_a_no_op():
+    assert call_prefill(m=0, ptrs=(None,) * 7) == mqa.MQA_OK

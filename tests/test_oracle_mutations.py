@@ -45,6 +45,9 @@ MUTANTS = [
     ("scale maps amax to 240", "scale = np.float32(amax / np.float32(E4M3FN_MAX))", "scale = np.float32(amax / np.float32(240.0))"),
     ("scale multiplies", "scaled = (k32 / scale).astype(np.float32)", "scaled = (k32 * scale).astype(np.float32)"),
     ("write ignores the slot", "rows[slot, :HEAD_DIM] = codes", "rows[i, :HEAD_DIM] = codes"),
+    ("prefill window end inclusive", "hi = min(max(int(ke[m]), 0), N)", "hi = min(max(int(ke[m]) + 1, 0), N)"),
+    ("prefill window start ignored", "lo = min(max(int(ks[m]), 0), N)", "lo = 0"),
+    ("prefill scale not applied", "x = score * scales[lo:hi, None]", "x = score"),
     ("top-k one short", "return np.sort(order[:min(k, values.size)])",
      "return np.sort(order[:min(k, values.size) - 1])"),
 ]
