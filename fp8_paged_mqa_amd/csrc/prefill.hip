@@ -8,23 +8,29 @@
 //
 // Mapping onto CDNA4. With many query rows the contraction is dense: the keys of a
 // 64-key stage serve every query row of a workgroup, so they are staged once in LDS,
-// already converted to f16 (exact) in the B-operand layout of v_mfma_f32_16x16x32_f16,
-// and the query rows stay in VGPRs as A operands (same byte-to-k assignment as the
-// paged kernel: lane (g, c) owns bytes [16g, 16g+16) and [64+16g, 64+16g+16) of its row).
-//   * Workgroup: 8 waves (two per SIMD), each owning QPW query rows (4 MFMA row tiles of
-//     16 heads). A grid of query blocks x key splits: splits are added when there are
-//     fewer query blocks than CUs. A workgroup computes the 64-key stages of its split
-//     that meet the union of its rows' windows and writes -inf over the rest of its
-//     split (nontemporal stores).
-//   * Stage pipeline: every thread loads 16 key bytes and its key's scale for the next
-//     stage into registers while the waves compute the current one from LDS; then the
-//     bytes are converted (the scale's sign folded into the fp8 sign bits, exact) and
-//     stored to LDS for the next round. Two barriers per stage.
-//   * LDS layout per 16-key tile: [k-step 0..3][lane 0..63][8 f16], so each k-step's B
+// already converted to f16 (exact) in the B-operand layout of v_mfma_f32_32x32x16_f16,
+// and the query rows stay in VGPRs as A operands. That shape is used because it
+// sustains about 1.6x the rate of the 16x16x32 f16 shape on gfx950 (a timed MFMA-only
+// loop: ~1.85 vs ~1.14 PFLOP/s).
+//   * A lane (h, j) of a 32x32 tile holds, for its row or column j, the 64 bytes
+//     [64h, 64h+64) of the 128-byte contraction, as eight 16-wide k-steps: the k order
+//     is permuted the same way on both operands, which leaves the dot products unchanged.
+//     A row tile is 32 heads of one query row (heads past H get weight 0); a wave holds
+//     two row tiles (two query rows at H <= 32, one at H = 48, 64).
+//   * Workgroup: 8 waves (two per SIMD). A grid of query blocks x key splits: splits are
+//     added until there are about four workgroups per CU. A workgroup computes the
+//     64-key stages of its split that meet the union of its rows' windows and writes
+//     -inf over the rest of its split (nontemporal stores).
+//   * Stage pipeline: two LDS buffers. While the waves compute stage s from one, every
+//     thread converts its 16 key bytes of stage s+1 (loaded during stage s-1; the
+//     scale's sign folded into the fp8 sign bits, exact) into the other and loads its
+//     bytes of stage s+2. One barrier per stage.
+//   * LDS layout per 32-key tile: [k-step 0..7][lane 0..63][8 f16], so each k-step's B
 //     operands are one conflict-free 1 KB ds_read_b128 per wave.
-//   * Epilogue as in the paged kernel: relu, weights, head sum per lane, two cross-lane
-//     swaps, times |scale|, window mask; a row's 64 logits of a stage leave in one
-//     256-byte store.
+//   * Epilogue: a lane's 16 results are heads 8q + 4h + r (q, r < 4) of key j; relu,
+//     weights and the head sum run in registers, one permlane32 swap adds the two lane
+//     halves, then |scale| and the window mask; a row's 64 logits of a stage leave as
+//     one 256-byte store.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -42,8 +48,8 @@ constexpr int kD = 128;
 constexpr int kWave = 64;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWave * kWaves;
-constexpr int kStage = 64;              // keys per stage: 4 MFMA column tiles
-constexpr int kTileBytes = 4 * 64 * 16;  // one 16-key tile of f16 B operands (4 KB)
+constexpr int kStage = 64;               // keys per stage: 2 MFMA column tiles of 32
+constexpr int kTileBytes = 8 * 64 * 16;  // one 32-key tile of f16 B operands (8 KB)
 
 struct Params {
   const uint8_t* q;     // [M, H, 128]
@@ -76,30 +82,28 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(int lo, int hi) {
   return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-struct Operand {
-  f16x8 k[4];
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// The 64 bytes a lane holds for one row (bytes [64h, 64h+64)) as the eight f16x8
+// operands of the chained 16-wide k-steps.
+struct Operand8 {
+  f16x8 k[8];
 };
 
-__device__ __forceinline__ float sum_lane_groups(float x) {
-  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-template <int TPJ, int QPW>
+// Query row tiles hold 32 heads (v_mfma_f32_32x32x16_f16): heads past H get weight 0.
+template <int T32, int QPW>
 __global__ __launch_bounds__(kThreads, 1) void prefill_logits_kernel(Params p) {
-  constexpr int TILES = TPJ * QPW;
-  static_assert(TILES <= 4, "query tile budget");
-  __shared__ __attribute__((aligned(16))) uint8_t bops[4 * kTileBytes];  // one stage: 16 KB
-  __shared__ float sabs[kStage];
+  constexpr int TILES = T32 * QPW;  // 32-head row tiles held by one wave
+  static_assert(TILES <= 2, "query tile budget");
+  __shared__ __attribute__((aligned(16))) uint8_t bops[2][2 * kTileBytes];  // two stages: 32 KB
+  __shared__ float sabs[2][kStage];
   __shared__ int win[2];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);
-  const int g = lane >> 4;
-  const int c = lane & 15;
-  const int M = p.M, N = p.N;
+  const int h = lane >> 5;   // lane half: k-bytes [64h, 64h+64) of its row; result rows 8q + 4h + r
+  const int j = lane & 31;   // head (A) / key (B) within a 32-wide tile
+  const int M = p.M, N = p.N, H = p.H;
   constexpr int QPG = kWaves * QPW;
   const int m0 = blockIdx.x * QPG;
   const int a = blockIdx.y * p.split_keys;
@@ -164,110 +168,130 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_logits_kernel(Params p) {
   fill(a, c0);
   fill(c1, b);
 
-  // Query rows as f16 A operands, weights.
-  Operand qa[TILES];
-  f32x4 wv[TILES];
+  // Query rows as f16 A operands: lane (h, j) holds bytes [64h, 64h+64) of head j of the
+  // tile, as the eight 8-element k-steps. Weights of the result rows 8q + 4h + r.
+  Operand8 qa[TILES];
+  f32x4 wv[TILES][4];
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
-    const int jl = t / TPJ, mm = t % TPJ;
+    const int jl = t / T32, mm = t % T32;
     const int m = min(mw + jl, M - 1);
-    const uint8_t* qr = p.q + ((int64_t)m * p.H + mm * 16 + c) * kD;
-    const i32x4 lo = load16(qr + 16 * g), hi = load16(qr + 64 + 16 * g);
-    qa[t].k[0] = fp8x8_to_f16(lo.x, lo.y);
-    qa[t].k[1] = fp8x8_to_f16(lo.z, lo.w);
-    qa[t].k[2] = fp8x8_to_f16(hi.x, hi.y);
-    qa[t].k[3] = fp8x8_to_f16(hi.z, hi.w);
-    wv[t] = *reinterpret_cast<const f32x4*>(p.w + (int64_t)m * p.H + mm * 16 + 4 * g);
+    const int head = min(mm * 32 + j, H - 1);  // heads past H: any row, weight 0
+    const uint8_t* qr = p.q + ((int64_t)m * H + head) * kD + 64 * h;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const i32x4 x = load16(qr + 16 * v);
+      qa[t].k[2 * v] = fp8x8_to_f16(x.x, x.y);
+      qa[t].k[2 * v + 1] = fp8x8_to_f16(x.z, x.w);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r0 = mm * 32 + 8 * q + 4 * h;  // rows r0 .. r0+3 of this lane's results
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wv[t][q][r] = r0 + r < H ? p.w[(int64_t)m * H + r0 + r] : 0.0f;
+    }
   }
 
-  // Stage loader: thread t holds bytes [16*(t%8), +16) of key t/8 of the stage.
-  const int lk = threadIdx.x >> 3;        // key of the stage, 0..63
-  const int lb = (threadIdx.x & 7) * 16;  // byte offset in the key's row
-  // Where those 16 bytes go: lane (g', c') = key % 16, k-steps 2*(lb >= 64) + {0, 1}.
-  const int dst_lane = ((lb & 63) >> 4) * 16 + (lk & 15);
-  const int dst_step = lb >= 64 ? 2 : 0;
-  uint8_t* const dst = bops + (lk >> 4) * kTileBytes + dst_step * 1024 + dst_lane * 16;
+  // Stage loader: thread t holds bytes [16*(t%8), +16) of key t/8 of the stage, i.e. the
+  // k-steps 2*(t%4), 2*(t%4)+1 of lane (h, j) = ((t%8)/4, key%32) of tile key/32.
+  const int lk = threadIdx.x >> 3;
+  const int lb = (threadIdx.x & 7) * 16;
+  const int dst_off = (lk >> 5) * kTileBytes + ((threadIdx.x & 3) * 2) * 1024 + ((lb >> 6) * 32 + (lk & 31)) * 16;
   auto fetch = [&](int s0, i32x4& raw, float& sc) {
     const int key = min(s0 + lk, N - 1);
     raw = load16(p.k + (int64_t)key * kD + lb);
     sc = p.ksc[key];
   };
-  auto stash = [&](i32x4 raw, float sc) {
+  auto stash = [&](int buf, i32x4 raw, float sc) {
     if (__float_as_int(sc) < 0) raw ^= (int)0x80808080;  // sign of the scale into the codes
-    const f16x8 f0 = fp8x8_to_f16(raw.x, raw.y);
-    const f16x8 f1 = fp8x8_to_f16(raw.z, raw.w);
-    *reinterpret_cast<f16x8*>(dst) = f0;
-    *reinterpret_cast<f16x8*>(dst + 1024) = f1;
-    if ((threadIdx.x & 7) == 0) sabs[lk] = __builtin_fabsf(sc);
+    *reinterpret_cast<f16x8*>(bops[buf] + dst_off) = fp8x8_to_f16(raw.x, raw.y);
+    *reinterpret_cast<f16x8*>(bops[buf] + dst_off + 1024) = fp8x8_to_f16(raw.z, raw.w);
+    if ((threadIdx.x & 7) == 0) sabs[buf][lk] = __builtin_fabsf(sc);
   };
 
+  // Double-buffered stages: stage s is computed from one LDS buffer while stage s+1,
+  // loaded into registers during stage s-1, is converted into the other; one barrier
+  // per stage. Key bytes run two stages ahead of their use.
   i32x4 raw;
   float sc;
   fetch(c0, raw, sc);
+  stash(0, raw, sc);
+  fetch(min(c0 + kStage, c1 - 1), raw, sc);
+  __syncthreads();
+  int buf = 0;
   for (int s0 = c0; s0 < c1; s0 += kStage) {
-    stash(raw, sc);
-    __syncthreads();
-    if (s0 + kStage < c1) fetch(s0 + kStage, raw, sc);  // next stage in flight meanwhile
+    const uint8_t* const bop = bops[buf];
+    const float* const sab = sabs[buf];
     float keep[QPW];
 #pragma unroll
     for (int jl = 0; jl < QPW; ++jl) keep[jl] = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      Operand kb;
+    for (int u = 0; u < 2; ++u) {  // two 32-key tiles per stage
+      Operand8 kb;
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        kb.k[st] = *reinterpret_cast<const f16x8*>(bops + u * kTileBytes + st * 1024 + lane * 16);
-      const float s = sabs[u * 16 + c];
-      f32x4 acc[TILES];
+      for (int st = 0; st < 8; ++st)
+        kb.k[st] = *reinterpret_cast<const f16x8*>(bop + u * kTileBytes + st * 1024 + lane * 16);
+      f32x16 acc[TILES];
 #pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[t].k[0], kb.k[0], f32x4{0, 0, 0, 0}, 0, 0, 0);
+      for (int t = 0; t < TILES; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t].k[0], kb.k[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-        for (int st = 1; st < 4; ++st)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[t].k[st], kb.k[st], acc[t], 0, 0, 0);
-      }
+      for (int st = 1; st < 8; ++st)
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t].k[st], kb.k[st], acc[t], 0, 0, 0);
+      const float s = sab[u * 32 + j];
 #pragma unroll
       for (int jl = 0; jl < QPW; ++jl) {
         float part = 0.0f;
 #pragma unroll
-        for (int mm = 0; mm < TPJ; ++mm) {
-          const int t = jl * TPJ + mm;
+        for (int mm = 0; mm < T32; ++mm) {
+          const int t = jl * T32 + mm;
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            part = __builtin_fmaf(wv[t][v], __builtin_elementwise_maximum(acc[t][v], 0.0f), part);
+          for (int v = 0; v < 16; ++v)
+            part = __builtin_fmaf(wv[t][v / 4][v % 4], __builtin_elementwise_maximum(acc[t][v], 0.0f), part);
         }
-        part = sum_lane_groups(part) * s;
-        if (g == u) keep[jl] = part;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        part = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * s;  // both halves: key 32u + j
+        if (h == u) keep[jl] = part;
       }
     }
-    const int t = s0 + lane;  // lane (g, c) stores key 16g + c of the stage
+    const int t = s0 + lane;  // lane (h, j) stores key 32h + j of the stage
     if (t < c1) {
 #pragma unroll
       for (int jl = 0; jl < QPW; ++jl)
         if (live[jl]) orow[jl][t] = (t >= lo_r[jl] && t < hi_r[jl]) ? keep[jl] : -__builtin_inff();
     }
-    __syncthreads();  // every wave is done with this stage's operands
+    if (s0 + kStage < c1) {  // next stage into the other buffer (last read two stages ago)
+      stash(buf ^ 1, raw, sc);
+      if (s0 + 2 * kStage < c1) fetch(s0 + 2 * kStage, raw, sc);
+    }
+    __syncthreads();
+    buf ^= 1;
   }
 }
 
 using KernelFn = void (*)(Params);
-constexpr KernelFn kTable[4] = {prefill_logits_kernel<1, 4>, prefill_logits_kernel<2, 2>,
-                                prefill_logits_kernel<3, 1>, prefill_logits_kernel<4, 1>};
+// [T32 - 1]: 32-head row tiles per query row (H = 16, 32 -> 1; 48, 64 -> 2).
+constexpr KernelFn kTable[2] = {prefill_logits_kernel<1, 2>, prefill_logits_kernel<2, 1>};
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
-  const int tpj = a.heads / 16;
-  const int qpw = tpj <= 2 ? 4 / tpj : 1;
+  const int t32 = (a.heads + 31) / 32;
+  const int qpw = t32 == 1 ? 2 : 1;
   const int qpg = kWaves * qpw;
   const int qblocks = (a.m + qpg - 1) / qpg;
   int cus = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  // Key splits so that there are at least as many workgroups as CUs (each split >= 4 stages).
+  // Key splits so that there are about four workgroups per CU (each split >= 4 stages):
+  // windows differ in length from row block to row block (causal prefill: by 2x), and
+  // with several workgroups per CU the dispatcher evens the load out.
   const int stages = (a.n + kStage - 1) / kStage;
-  int splits = qblocks >= cus ? 1 : (cus + qblocks - 1) / qblocks;
+  const int target = 4 * cus;
+  int splits = qblocks >= target ? 1 : (target + qblocks - 1) / qblocks;
   const int max_splits = (stages + 3) / 4;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -286,7 +310,7 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   p.N = a.n;
   p.H = a.heads;
   p.split_keys = split_stages * kStage;
-  hipLaunchKernelGGL(kTable[tpj - 1], dim3((unsigned)qblocks, (unsigned)splits), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(kTable[t32 - 1], dim3((unsigned)qblocks, (unsigned)splits), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
