@@ -312,3 +312,116 @@ def page_random_bytes_case(ctx_len: int, seed: int = 42, heads: int = 32,
     return Workload(name=f"random-bytes ctx={ctx_len}", q=q, kv_cache=kv, weights=w,
                     context_lens=np.array([ctx_len], dtype=np.int32), block_tables=bt,
                     max_model_len=max_model_len, next_n=1)
+
+
+# ---------------------------------------------------------------------------
+# Sparse MLA decode inputs: latent rows of 576 e4m3fn codes (512 compressed + 64 rotary
+# dims), 16 query heads per row, per-tensor fp32 scales, and per-row position lists of
+# the shape the indexer's top-k emits (min(topk, visible) distinct positions in any
+# order, then -1 padding).
+
+MLA_KV_DIM = 576
+MLA_HEADS = 16
+MLA_SM_SCALE = float(np.float32(1.0 / np.sqrt(192.0)))  # 1/sqrt(128 + 64): DeepSeek-V3 head dims
+MLA_Q_SCALE = 0.75
+MLA_KV_SCALE = 1.25
+
+
+@dataclass
+class MlaCase:
+    name: str
+    next_n: int
+    q: np.ndarray             # uint8 [B*N, 16, 576]
+    kv_cache: np.ndarray      # uint8 [num_slots, 576] or [num_blocks, S, 576]
+    block_tables: np.ndarray  # int32 [B, W]
+    indices: np.ndarray       # int32 [B*N, topk]
+    context_lens: np.ndarray  # int32 [B]
+    q_scale: float
+    kv_scale: float
+    sm_scale: float
+
+    @property
+    def batch(self) -> int:
+        return int(self.block_tables.shape[0])
+
+    @property
+    def rows(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def topk(self) -> int:
+        return int(self.indices.shape[1])
+
+    @property
+    def block_size(self) -> int:
+        return 1 if self.kv_cache.ndim == 2 else int(self.kv_cache.shape[1])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.kv_cache.shape[0])
+
+    @property
+    def listed(self) -> int:
+        return int((self.indices >= 0).sum())
+
+
+def make_mla_case(*, batch, next_n, ctx, topk=TOPK, block_size=1, seed=0, pool=None, table="permuted",
+                  poison_unused=True, q_scale=MLA_Q_SCALE, kv_scale=MLA_KV_SCALE, sm_scale=MLA_SM_SCALE,
+                  table_width=None, outlier_rows=0.0) -> MlaCase:
+    """Seeded sparse-MLA inputs. ctx counts tokens of each request (the N query tokens
+    included); row j of request b lists min(topk, ctx - N + j + 1) distinct positions of
+    its visible prefix in random order. ``pool`` counts blocks of ``block_size`` tokens.
+    Unreferenced cache rows hold NaN codes when ``poison_unused``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ctx = np.broadcast_to(np.asarray(ctx, dtype=np.int64), (batch,)).copy()
+    S = int(block_size)
+    nblk = (ctx + S - 1) // S
+    W = int(table_width or max(1, int(nblk.max(initial=1))))
+    if pool is None:
+        pool = max(1, int(nblk.sum()))
+    if table == "permuted":
+        perm = rng.permutation(pool)
+        tables = np.full((batch, W), -1, dtype=np.int64)
+        off = 0
+        for b in range(batch):
+            tables[b, :nblk[b]] = perm[off:off + nblk[b]]
+            off += int(nblk[b])
+        assert off <= pool, "pool too small"
+    elif table == "identity":
+        tables = np.tile(np.arange(W, dtype=np.int64), (batch, 1))
+        assert W <= pool
+    else:
+        raise ValueError(table)
+    q = to_e4m3fn_bytes(rng.standard_normal((batch * next_n, MLA_HEADS, MLA_KV_DIM), dtype=np.float32))
+    vals = rng.standard_normal((pool * S, MLA_KV_DIM), dtype=np.float32)
+    if outlier_rows:
+        vals[rng.random(pool * S) < outlier_rows] *= 8.0
+    rows = to_e4m3fn_bytes(vals)
+    idx = np.full((batch * next_n, topk), -1, dtype=np.int64)
+    used = np.zeros(pool * S, dtype=bool)
+    for b in range(batch):
+        for j in range(next_n):
+            vis = max(0, int(ctx[b]) - next_n + j + 1)
+            n = min(topk, vis)
+            pos = rng.choice(vis, size=n, replace=False) if n else np.zeros(0, np.int64)
+            idx[b * next_n + j, :n] = pos
+            if n:
+                used[tables[b][pos // S] * S + pos % S] = True
+    if poison_unused:
+        rows[~used] = 0x7F
+    kv = rows if S == 1 else rows.reshape(pool, S, MLA_KV_DIM)
+    return MlaCase(f"mla b{batch} n{next_n} topk{topk} S{S} seed{seed}", next_n, q, kv,
+                   tables.astype(np.int32), idx.astype(np.int32), ctx.astype(np.int32),
+                   float(np.float32(q_scale)), float(np.float32(kv_scale)), float(np.float32(sm_scale)))
+
+
+def make_mla_workload(*, poison_unused=False, seed=None) -> MlaCase:
+    """Sparse MLA decode behind the indexer's decode workload of 64 requests, N = 1,
+    ctx ~ U{1..8192} (2047, 2048, 2049, 4096, 4097 forced): each row attends its
+    min(2048, ctx) selected positions, gathered through a random permutation of a
+    600 000-row latent cache (one token per block)."""
+    rng = np.random.Generator(np.random.PCG64(4242 if seed is None else seed))
+    ctx = rng.integers(1, 8193, size=64)
+    ctx[:5] = [2047, 2048, 2049, 4096, 4097]
+    return make_mla_case(batch=64, next_n=1, ctx=ctx, topk=TOPK, pool=600_000, table_width=8192,
+                         seed=int(rng.integers(1 << 31)), poison_unused=poison_unused)

@@ -83,3 +83,56 @@ def test_unmutated_oracle_passes_every_pin():
     mod = types.ModuleType("oracle_copy")
     exec(compile(text, SRC, "exec"), mod.__dict__)
     assert _caught(mod) is None
+
+
+# Sparse MLA decode oracle: planted mistakes must be caught by its own pins.
+from pins_mla import MLA_PINS  # noqa: E402
+
+MLA_SRC = os.path.join(os.path.dirname(SRC), "sparse_mla_oracle.py")
+
+MLA_MUTANTS = [
+    ("softmax scale dropped", "c = float(np.float32(sm_scale)) * float(np.float32(q_scale))", "c = float(np.float32(q_scale))"),
+    ("q scale dropped", "c = float(np.float32(sm_scale)) * float(np.float32(q_scale))", "c = float(np.float32(sm_scale))"),
+    ("values not scaled", "out[r] = vs * (p.T @ keys[:, :MLA_V_DIM])", "out[r] = p.T @ keys[:, :MLA_V_DIM]"),
+    ("values from the wrong dims", "out[r] = vs * (p.T @ keys[:, :MLA_V_DIM])", "out[r] = vs * (p.T @ keys[:, 64:])"),
+    ("softmax over heads", "l = e.sum(axis=0)\n        p = e / l", "l = e.sum(axis=1, keepdims=True)\n        p = e / l"),
+    ("maximum not subtracted", "e = np.exp(score - m)\n        l = e.sum(axis=0)\n        p = e / l",
+     "e = np.exp(score)\n        l = e.sum(axis=0)\n        p = e / l"),
+    ("lse without the maximum", "lse[r] = m + np.log(l)", "lse[r] = np.log(l)"),
+    ("padding attended", "pos = idx[r][idx[r] >= 0]\n        if pos.size == 0:\n            continue\n        if pos.max()",
+     "pos = idx[r]\n        if pos.size == 0:\n            continue\n        if pos.max()"),
+    ("duplicates collapsed", "pos = idx[r][idx[r] >= 0]\n        if pos.size == 0:\n            continue\n        if pos.max()",
+     "pos = np.unique(idx[r][idx[r] >= 0])\n        if pos.size == 0:\n            continue\n        if pos.max()"),
+    ("block slot ignored", "return entries * block_size + t % block_size", "return entries * block_size"),
+    ("request of a row taken modulo", "b = r // next_n\n        pos", "b = r % next_n\n        pos"),
+    ("query of row 0 for every row", "score = (keys @ qv[r].T) * c", "score = (keys @ qv[0].T) * c"),
+]
+
+
+def _load_mla_mutant(old, new):
+    with open(MLA_SRC) as f:
+        text = f.read()
+    assert old in text, f"mutation site not found: {old!r}"
+    text = text.replace(old, new).replace("from .mqa_oracle import", "from oracle.mqa_oracle import")
+    mod = types.ModuleType("mla_oracle_mutant")
+    mod.__file__ = MLA_SRC
+    exec(compile(text, MLA_SRC + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+def _mla_caught(mod):
+    for pin in MLA_PINS:
+        try:
+            pin(mod)
+        except Exception:
+            return pin.__name__
+    return None
+
+
+@pytest.mark.parametrize("desc,old,new", MLA_MUTANTS, ids=[m[0] for m in MLA_MUTANTS])
+def test_mla_pins_catch_mutant(desc, old, new):
+    assert _mla_caught(_load_mla_mutant(old, new)) is not None, f"no pin catches: {desc}"
+
+
+def test_unmutated_mla_oracle_passes_every_pin():
+    assert _mla_caught(_load_mla_mutant("MLA_V_DIM = 512", "MLA_V_DIM = 512")) is None
