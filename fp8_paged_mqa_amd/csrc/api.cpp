@@ -40,6 +40,23 @@ int check_shape(const mqa_shape* s, int32_t max_model_len) {
   return MQA_OK;
 }
 
+constexpr int32_t kMlaHeads = 16, kMlaDim = 576, kMlaVDim = 512;
+constexpr int32_t kMlaMaxRows = 65535;   // grid dimension of the row index
+constexpr int32_t kMlaMaxTopk = 1 << 20;
+
+int check_mla_shape(const mqa_mla_shape* s) {
+  if (s == nullptr) return MQA_ERR_NULL;
+  if (s->batch < 0 || s->next_n < 1 || s->topk < 1 || s->block_size < 1 || s->block_table_stride < 1 ||
+      s->num_blocks < 1 || s->heads < 1 || s->head_dim < 1 || s->v_dim < 1)
+    return MQA_ERR_SHAPE;
+  if (s->heads != kMlaHeads || s->head_dim != kMlaDim || s->v_dim != kMlaVDim) return MQA_ERR_UNSUPPORTED;
+  if (s->block_size > kMaxBlockSize || (s->block_size & (s->block_size - 1)) != 0) return MQA_ERR_UNSUPPORTED;
+  if ((int64_t)s->block_table_stride * s->block_size > INT32_MAX) return MQA_ERR_UNSUPPORTED;
+  if (s->num_blocks > INT32_MAX / s->block_size) return MQA_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * s->next_n > kMlaMaxRows || s->topk > kMlaMaxTopk) return MQA_ERR_UNSUPPORTED;
+  return MQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -54,7 +71,8 @@ const char* mqa_status_string(int status) {
              "block_table_stride * block_size and, for block_size > 1, num_blocks * block_size "
              "below 2^31), heads a multiple of 16 up to 128, "
              "next_n 1..4, max_model_len <= 2^30, batch <= 8192 for the logits, k 1..2048, 16-byte aligned q and weights, "
-             "4-byte aligned kv_cache, logits, idx and integer arrays";
+             "4-byte aligned kv_cache, logits, idx and integer arrays; sparse MLA decode: heads 16, "
+             "head_dim 576, v_dim 512, rows <= 65535, topk <= 2^20, 16-byte aligned q, kv_cache, out and workspace";
     case MQA_ERR_WORKSPACE: return "workspace missing or too small";
     case MQA_ERR_HIP: return "HIP launch error";
     default: return "unknown status";
@@ -163,6 +181,46 @@ int mqa_indexer_k_write(const void* k, int32_t k_dtype, int64_t num_tokens, cons
   a.num_slots = num_slots;
   a.bf16 = k_dtype == MQA_DTYPE_BF16;
   return mqa::launch_k_write(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+size_t mqa_sparse_mla_workspace_bytes(const mqa_mla_shape* shape) {
+  if (check_mla_shape(shape) != MQA_OK) return 0;
+  return mqa::sparse_mla_plan((int64_t)shape->batch * shape->next_n, shape->topk).workspace_bytes;
+}
+
+int mqa_sparse_mla_decode(const uint8_t* q, float q_scale, const uint8_t* kv_cache, float kv_scale,
+                          const int32_t* indices, const int32_t* block_tables, float sm_scale, float* out,
+                          float* lse, const mqa_mla_shape* shape, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  const int st = check_mla_shape(shape);
+  if (st != MQA_OK) return st;
+  const int64_t rows = (int64_t)shape->batch * shape->next_n;
+  if (rows == 0) return MQA_OK;
+  if (!q || !kv_cache || !indices || !block_tables || !out) return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(indices, 4) ||
+      !aligned(block_tables, 4) || (lse && !aligned(lse, 4)) || (workspace && !aligned(workspace, 16)))
+    return MQA_ERR_UNSUPPORTED;
+  const mqa::SparseMlaPlan plan = mqa::sparse_mla_plan(rows, shape->topk);
+  if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+    return MQA_ERR_WORKSPACE;
+  mqa::SparseMlaLaunch a;
+  a.q = q;
+  a.kv = kv_cache;
+  a.indices = indices;
+  a.bt = block_tables;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.q_scale = q_scale;
+  a.kv_scale = kv_scale;
+  a.sm_scale = sm_scale;
+  a.rows = rows;
+  a.num_blocks = shape->num_blocks;
+  a.next_n = shape->next_n;
+  a.topk = shape->topk;
+  a.bt_stride = shape->block_table_stride;
+  a.block_shift = log2_exact(shape->block_size);
+  return mqa::launch_sparse_mla(a, plan, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
 }  // extern "C"

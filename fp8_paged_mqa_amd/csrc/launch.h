@@ -56,6 +56,31 @@ struct KWriteLaunch {
 // Enqueue the K-cache write on `stream`.
 hipError_t launch_k_write(const KWriteLaunch& a, hipStream_t stream);
 
+struct SparseMlaLaunch {
+  const uint8_t* q;        // [rows, 16, 576] e4m3fn
+  const uint8_t* kv;       // [num_blocks * block_size, 576] e4m3fn
+  const int32_t* indices;  // [rows, topk] positions, negative = padding
+  const int32_t* bt;       // [batch, bt_stride]
+  float* out;              // [rows, 16, 512]
+  float* lse;              // [rows, 16] or null
+  void* workspace;         // SparseMlaPlan::workspace_bytes, 16-byte aligned
+  float q_scale, kv_scale, sm_scale;
+  int64_t rows, num_blocks;
+  int32_t next_n, topk, bt_stride, block_shift;
+};
+
+struct SparseMlaPlan {
+  int32_t splits = 1, tiles_per_split = 1;
+  size_t workspace_bytes = 0;
+};
+
+// Split of each row's list over workgroups for the current device, and the workspace
+// it needs.
+SparseMlaPlan sparse_mla_plan(int64_t rows, int32_t topk);
+
+// Enqueue the sparse MLA decode (and the split merge when plan.splits > 1).
+hipError_t launch_sparse_mla(const SparseMlaLaunch& a, const SparseMlaPlan& plan, hipStream_t stream);
+
 // Device scratch the top-k launch needs for `rows` rows of length max_model_len
 // (0 when every row fits one workgroup).
 size_t topk_workspace_bytes(int64_t rows, int32_t max_model_len);

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa.so")
 MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED, MQA_ERR_WORKSPACE, MQA_ERR_HIP = range(6)
 
 EXPORTS = ("mqa_paged_logits", "mqa_topk", "mqa_topk_workspace_bytes", "mqa_status_string",
-           "mqa_indexer_k_write", "mqa_logits")
+           "mqa_indexer_k_write", "mqa_logits", "mqa_sparse_mla_decode", "mqa_sparse_mla_workspace_bytes")
 MQA_DTYPE_BF16, MQA_DTYPE_F32 = 0, 1
 
 
@@ -26,6 +26,12 @@ class mqa_shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("next_n", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("block_table_stride", ctypes.c_int32), ("num_blocks", ctypes.c_int64)]
+
+
+class mqa_mla_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("next_n", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("block_table_stride", ctypes.c_int32), ("topk", ctypes.c_int32), ("num_blocks", ctypes.c_int64)]
 
 
 class MqaError(RuntimeError):
@@ -53,6 +59,12 @@ def _load() -> ctypes.CDLL:
     lib.mqa_indexer_k_write.restype = ctypes.c_int
     lib.mqa_logits.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
     lib.mqa_logits.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    mshp = ctypes.POINTER(mqa_mla_shape)
+    lib.mqa_sparse_mla_decode.argtypes = [vp, f32, vp, f32, vp, vp, f32, vp, vp, mshp, vp, sz, vp]
+    lib.mqa_sparse_mla_decode.restype = ctypes.c_int
+    lib.mqa_sparse_mla_workspace_bytes.argtypes = [mshp]
+    lib.mqa_sparse_mla_workspace_bytes.restype = sz
     return lib
 
 
@@ -143,6 +155,37 @@ def mqa_indexer_k_write(k, slot_mapping, kv_cache, stream=None, check: bool = Tr
                                   int(num_slots), _stream(stream))
     if check and st != MQA_OK:
         raise MqaError(st, "mqa_indexer_k_write")
+    return st
+
+
+def mla_shape_of(q, kv_cache, block_tables, indices, next_n=1) -> mqa_mla_shape:
+    """Shape struct from tensors laid out as the header describes: q [B*N, 16, 576],
+    kv_cache [num_slots, 576] (block_size 1) or [num_blocks, S, (1,) 576], block_tables
+    [B, W], indices [B*N, topk]."""
+    rows, heads, dim = q.shape
+    bs = kv_cache.shape[1] if kv_cache.dim() >= 3 else 1
+    return mqa_mla_shape(int(block_tables.shape[0]), int(next_n), int(heads), int(dim), 512, int(bs),
+                         int(block_tables.shape[1]), int(indices.shape[1]), int(kv_cache.shape[0]))
+
+
+def mqa_sparse_mla_workspace_bytes(shape: mqa_mla_shape) -> int:
+    return int(_lib.mqa_sparse_mla_workspace_bytes(ctypes.byref(shape)))
+
+
+def mqa_sparse_mla_decode(q, q_scale, kv_cache, kv_scale, indices, block_tables, sm_scale, out, lse=None,
+                          shape: mqa_mla_shape | None = None, workspace=None, next_n=1, stream=None,
+                          check: bool = True) -> int:
+    """out[B*N, 16, 512] (and lse[B*N, 16]) <- attention of each row over its listed
+    positions. q uint8 [B*N,16,576], kv_cache uint8 (576-byte rows), indices int32
+    [B*N, topk], block_tables int32 [B, W]; out / lse float32."""
+    if shape is None:
+        shape = mla_shape_of(q, kv_cache, block_tables, indices, next_n)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.mqa_sparse_mla_decode(_ptr(q), float(q_scale), _ptr(kv_cache), float(kv_scale), _ptr(indices),
+                                    _ptr(block_tables), float(sm_scale), _ptr(out), _ptr(lse), ctypes.byref(shape),
+                                    _ptr(workspace), ws_bytes, _stream(stream))
+    if check and st != MQA_OK:
+        raise MqaError(st, "mqa_sparse_mla_decode")
     return st
 
 

@@ -193,6 +193,72 @@ enum { MQA_DTYPE_BF16 = 0, MQA_DTYPE_F32 = 1 };
 int mqa_indexer_k_write(const void* k, int32_t k_dtype, int64_t num_tokens, const int64_t* slot_mapping,
                         uint8_t* kv_cache, int64_t num_slots, hipStream_t stream);
 
+/*
+ * Shape of a sparse MLA decode call. rows = batch * next_n query rows; row r = b*N + j
+ * belongs to request b.
+ */
+typedef struct mqa_mla_shape {
+  int32_t batch;              /* B requests */
+  int32_t next_n;             /* N query tokens per request (1..4 in the pages' use; any >= 1) */
+  int32_t heads;              /* query heads per row: 16 */
+  int32_t head_dim;           /* latent row width in bytes / codes: 576 */
+  int32_t v_dim;              /* value width: 512 (the first 512 dims of a latent row) */
+  int32_t block_size;         /* S tokens per cache block, a power of two up to 65536 */
+  int32_t block_table_stride; /* W entries per block-table row */
+  int32_t topk;               /* entries per row of indices */
+  int64_t num_blocks;         /* blocks in kv_cache */
+} mqa_mla_shape;
+
+/*
+ * mqa_sparse_mla_decode - attention of each decode row over the positions the indexer
+ * selected for it (sparse MLA decode).
+ *
+ * Sources: the stepcodex.com pa_mqa_logits issue, "Downstream impact" (the positions the
+ * top-k keeps are the ones the sparse attention attends); the chat-gpts.plus summary
+ * (post 69330) of the aiter MLA decode issue, "问题场景" and "环境排查" (fp8 q and KV cache,
+ * 16 query heads per latent KV head, 1 to 4 query tokens per request); vLLM pull request
+ * 31282, "The Bug" (one token per cache page). The pages leave the row width, the scale
+ * placement and the list form open; this call reads them as:
+ *   q            [rows, 16, 576] e4m3fn codes, dequantised as code * q_scale
+ *   kv_cache     [num_blocks, S, 576] e4m3fn codes (576 = 512 compressed + 64 rotary dims,
+ *                DeepSeek-V3's sizes), dequantised as code * kv_scale
+ *   indices      [rows, topk] int32 positions of request b (the layout mqa_topk writes);
+ *                a negative entry is padding; a position listed twice is attended twice
+ *   block_tables [B, W] int32: position t is slot t % S of block block_tables[b*W + t/S]
+ * and computes, over the row's listed positions t,
+ *   score(h, t) = sm_scale * q_scale * kv_scale * (q[r,h,:] . k_t)
+ *   out[(r*16 + h)*512 + c] = kv_scale * sum_t softmax_t(score(h, .)) * k_t[c], c < 512
+ *   lse[r*16 + h] = log(sum_t exp(score(h, t)))   (natural log; lse may be NULL)
+ * A row with no listed position gets out = 0 and lse = -inf. A listed position at or past
+ * W*S, or whose block-table entry lies outside [0, num_blocks), makes its row NaN (out and
+ * lse); no access leaves the described buffers.
+ *
+ * Precision: the 576-term dot products are exact (fp8 codes as f16, fp32 accumulation of
+ * exact products, rounded as the hardware sums them); softmax in fp32 with probabilities
+ * rounded to f16 (relative 2^-11) for the value contraction.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller; shape is a host
+ * struct. workspace (16-byte aligned, at least mqa_sparse_mla_workspace_bytes(shape)
+ * bytes; may be NULL when that is 0) holds per-split partial results and is fully
+ * rewritten by each call. Nothing is allocated or synchronised; the work is enqueued on
+ * stream (capturable into a graph).
+ *
+ * Errors: MQA_ERR_NULL (shape, q, kv_cache, indices, block_tables or out NULL with rows >
+ * 0), MQA_ERR_SHAPE (negative batch, next_n, topk, block_size, stride or num_blocks < 1),
+ * MQA_ERR_UNSUPPORTED (heads != 16, head_dim != 576, v_dim != 512, block_size not a power
+ * of two up to 65536, W*S or num_blocks*S at or above 2^31, rows > 65535, topk > 2^20,
+ * q / kv_cache / out / workspace not 16-byte aligned, indices / block_tables / lse not
+ * 4-byte aligned), MQA_ERR_WORKSPACE, MQA_ERR_HIP.
+ */
+int mqa_sparse_mla_decode(const uint8_t* q, float q_scale, const uint8_t* kv_cache, float kv_scale,
+                          const int32_t* indices, const int32_t* block_tables, float sm_scale, float* out,
+                          float* lse, const mqa_mla_shape* shape, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Workspace size for mqa_sparse_mla_decode with this shape on the current device (0 when
+ * none is needed or the shape is invalid). */
+size_t mqa_sparse_mla_workspace_bytes(const mqa_mla_shape* shape);
+
 /* Workspace size for mqa_topk with this shape, L and k (0 when the shape is invalid). */
 size_t mqa_topk_workspace_bytes(const mqa_shape* shape, int32_t max_model_len, int32_t k);
 

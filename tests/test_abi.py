@@ -180,3 +180,68 @@ def test_prefill_logits_rejects(kw, status):
 
 def test_prefill_zero_rows_is_a_no_op():
     assert call_prefill(m=0, ptrs=(None,) * 7) == mqa.MQA_OK
+
+
+def mla_shape(**kw):
+    base = dict(batch=2, next_n=2, heads=16, head_dim=576, v_dim=512, block_size=1, block_table_stride=100,
+                topk=64, num_blocks=1000)
+    base.update(kw)
+    return mqa.mqa_mla_shape(*(base[f] for f, _ in mqa.mqa_mla_shape._fields_))
+
+
+def call_mla(shape=None, ptrs=None, lse=None, ws=None, ws_bytes=0):
+    q, kv, idx, bt, out = ptrs if ptrs is not None else (FAKE,) * 5
+    shp = None if shape is None else ctypes.byref(shape)
+    return mqa._lib.mqa_sparse_mla_decode(q, 1.0, kv, 1.0, idx, bt, 0.07, out, lse, shp, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), mqa.MQA_ERR_SHAPE),
+    (dict(next_n=0), mqa.MQA_ERR_SHAPE),
+    (dict(topk=0), mqa.MQA_ERR_SHAPE),
+    (dict(block_size=0), mqa.MQA_ERR_SHAPE),
+    (dict(block_table_stride=0), mqa.MQA_ERR_SHAPE),
+    (dict(num_blocks=0), mqa.MQA_ERR_SHAPE),
+    (dict(heads=32), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(head_dim=512), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(v_dim=576), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(block_size=3), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(block_size=1 << 17), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(block_size=64, block_table_stride=1 << 25), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(block_size=64, num_blocks=1 << 25), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(batch=65536, next_n=1), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(topk=(1 << 20) + 1), mqa.MQA_ERR_UNSUPPORTED),
+])
+def test_sparse_mla_rejects_shapes(kw, status):
+    assert call_mla(mla_shape(**kw)) == status
+
+
+def test_sparse_mla_rejects_pointers():
+    assert call_mla(None) == mqa.MQA_ERR_NULL
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        assert call_mla(mla_shape(), tuple(ptrs)) == mqa.MQA_ERR_NULL, i
+    for i in (0, 1, 4):  # q, kv_cache, out: 16-byte alignment
+        ptrs = [FAKE] * 5
+        ptrs[i] = ctypes.c_void_p(0x10008)
+        assert call_mla(mla_shape(), tuple(ptrs)) == mqa.MQA_ERR_UNSUPPORTED, i
+    for i in (2, 3):  # indices, block_tables: 4-byte alignment
+        ptrs = [FAKE] * 5
+        ptrs[i] = ctypes.c_void_p(0x10002)
+        assert call_mla(mla_shape(), tuple(ptrs)) == mqa.MQA_ERR_UNSUPPORTED, i
+    assert call_mla(mla_shape(), lse=ctypes.c_void_p(0x10002)) == mqa.MQA_ERR_UNSUPPORTED
+
+
+def test_sparse_mla_zero_rows_is_a_no_op():
+    assert call_mla(mla_shape(batch=0), (None,) * 5) == mqa.MQA_OK
+
+
+def test_sparse_mla_workspace():
+    big = mla_shape(batch=64, next_n=1, topk=2048)
+    need = mqa.mqa_sparse_mla_workspace_bytes(big)
+    assert need > 0 and need % (4 * (16 * 512 + 32)) == 0
+    assert call_mla(big) == mqa.MQA_ERR_WORKSPACE
+    assert call_mla(big, ws=FAKE, ws_bytes=need - 1) == mqa.MQA_ERR_WORKSPACE
+    assert mqa.mqa_sparse_mla_workspace_bytes(mla_shape(batch=1, next_n=1, topk=64)) == 0
+    assert mqa.mqa_sparse_mla_workspace_bytes(mla_shape(heads=8)) == 0
