@@ -3,6 +3,7 @@
     python bench.py [--steps K] [--warmup W] [--config 1..5] [--block-size S] [--no-cpu-baseline]
     python bench.py --op kwrite [--tokens T]   (the K-cache write alone; not the default line)
     python bench.py --op prefill [--m M --n N --heads H]   (non-paged logits; not the default line)
+    python bench.py --op mla   (sparse MLA decode over the selected positions; not the default line)
 
 One step = mqa_paged_logits + mqa_topk over one batch of the named synthetic workload,
 inputs already resident in HBM. Steps are captured into a HIP graph and replayed (the
@@ -199,6 +200,69 @@ def bench_kwrite(args):
                      "algorithmic_bytes": nbytes, "traffic": None}}), flush=True)
 
 
+def bench_mla(args):
+    """Attended positions/s of mqa_sparse_mla_decode on the decode workload behind the
+    indexer's headline shape: 64 requests, N = 1, each row attending its min(2048, ctx)
+    selected positions (ctx ~ U{1..8192}) of a 600 000-row latent cache (576-byte rows,
+    one token per block, random permutation), 16 heads. Graph replays over rotating copies."""
+    import torch
+    sys.path.insert(0, ROOT)
+    from fp8_paged_mqa_amd import mqa, workloads
+    case = workloads.make_mla_workload(poison_unused=False)
+    C = max(1, args.copies)
+    dev = "cuda"
+    q_h, kv_h = torch.from_numpy(case.q), torch.from_numpy(case.kv_cache)
+    idx_h, bt_h = torch.from_numpy(case.indices), torch.from_numpy(case.block_tables)
+    copies = []
+    for _ in range(C):
+        q, kv, idx, bt = q_h.to(dev), kv_h.to(dev), idx_h.to(dev), bt_h.to(dev)
+        shape = mqa.mla_shape_of(q, kv, bt, idx, case.next_n)
+        nbytes = mqa.mqa_sparse_mla_workspace_bytes(shape)
+        copies.append(dict(q=q, kv=kv, idx=idx, bt=bt, shape=shape,
+                           ws=torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev),
+                           out=torch.empty((case.rows, 16, 512), dtype=torch.float32, device=dev),
+                           lse=torch.empty((case.rows, 16), dtype=torch.float32, device=dev)))
+    def run(c):
+        mqa.mqa_sparse_mla_decode(c["q"], case.q_scale, c["kv"], case.kv_scale, c["idx"], c["bt"], case.sm_scale,
+                                  c["out"], c["lse"], shape=c["shape"], workspace=c["ws"])
+    for i in range(4):
+        run(copies[i % C])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(C):
+            run(copies[i])
+    for _ in range(max(1, args.warmup // C)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // C)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * C)
+    listed, rows, topk = case.listed, case.rows, case.topk
+    # Algorithmic bytes: each listed row once, the index list, one table entry per listed
+    # position, the queries, the outputs and lse. The splits' partial states are extra.
+    nbytes = 576 * listed + 4 * rows * topk + 4 * listed + rows * 16 * 576 + rows * 16 * 512 * 4 + rows * 16 * 4
+    ws_bytes = mqa.mqa_sparse_mla_workspace_bytes(copies[0]["shape"])
+    achieved = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "sparse MLA decode: attended positions/s (16 heads, 576-dim fp8 latent rows)",
+        "value": listed / (us * 1e-6), "unit": "positions/s", "n_gpus": 1, "steps": reps * C,
+        "warmup": args.warmup, "us_per_call": us, "higher_is_better": True,
+        "dtype": "fp8e4m3fn->f16 mfma, f32 softmax", "data": "synthetic",
+        "config": {"workload": "64 requests, N=1, min(2048, ctx) positions per row, ctx~U{1..8192}, "
+                               "600000-row latent cache, permuted", "rows": rows, "topk": topk, "listed": listed,
+                   "input_copies": C},
+        "partial_state_bytes": 2 * ws_bytes,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "kernel": "sparse_mla_kernel + sparse_mla_combine_kernel",
+                     "algorithmic_bytes": nbytes, "traffic": None}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,7 +273,7 @@ def main():
     ap.add_argument("--block-size", type=int, default=1,
                     help="tokens per KV block (1: the pages' layout; the default line uses 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="step", choices=["step", "kwrite", "prefill"])
+    ap.add_argument("--op", default="step", choices=["step", "kwrite", "prefill", "mla"])
     ap.add_argument("--m", type=int, default=4096, help="query rows for --op prefill")
     ap.add_argument("--n", type=int, default=8192, help="keys for --op prefill")
     ap.add_argument("--heads", type=int, default=32, help="heads for --op prefill")
@@ -226,6 +290,9 @@ def main():
         return
     if args.op == "prefill":
         bench_prefill(args)
+        return
+    if args.op == "mla":
+        bench_mla(args)
         return
 
     import torch

@@ -71,7 +71,6 @@ constexpr float kPScale = 32768.0f;          // probabilities are kept as p * 2^
 constexpr float kLn2 = 0.69314718055994531f;
 static_assert(kTileBytes % 1024 == 0, "tile = whole 1 KB wave loads");
 
-enum : int { kValid = 0, kPad = 1, kBad = 2 };
 
 struct Params {
   const uint8_t* q;      // [R, 16, 576]
@@ -94,7 +93,8 @@ struct Smem {
   float s[kH * kSStride];        // scores of the tile, [head][token]
   float wmax[kWaves][kH];
   int32_t rows[kMaxTiles][kTile];  // row to load for each token of each live tile
-  uint8_t stat[kMaxTiles][kTile];  // kValid / kPad / kBad
+  uint64_t padm[kMaxTiles];        // bit u: token u of the tile is padding
+  uint64_t badm[kMaxTiles];        // bit u: token u names a position outside the cache
   int32_t live[kMaxTiles];         // list tile of each live tile
   int32_t nlive;
 };
@@ -210,53 +210,58 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
     }
   }
 
-  // Resolve every listed position of this split to a cache row (wave t resolves list
-  // tiles t, t+4; live tiles are compacted by wave 0).
+  // Resolve every listed position of this split to a cache row. Wave w takes list tiles
+  // w and w+4: both index loads, then both table loads, so two round trips in all.
+  static_assert(kMaxTiles == 2 * kWaves, "two list tiles per wave");
   const uint32_t cap = (uint32_t)p.W << p.bshift;
   const int smask = (1 << p.bshift) - 1;
-  for (int t = wave; t < ntiles; t += kWaves) {
-    const int e = e0 + t * kTile + lane;
-    const int pos = e < p.topk ? p.idx[(int64_t)r * p.topk + e] : -1;
-    int st = kPad, row = 0;
-    if (pos >= 0) {
-      if ((uint32_t)pos >= cap) {
-        st = kBad;
-      } else {
-        const int ent = p.bt[(int64_t)b * p.W + (pos >> p.bshift)];
-        if (ent < 0 || (uint32_t)ent >= p.nblk) st = kBad;
-        else { st = kValid; row = (ent << p.bshift) | (pos & smask); }
+  int pos[2], ent[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = e0 + (wave + kWaves * h) * kTile + lane;
+    pos[h] = (wave + kWaves * h < ntiles && e < p.topk) ? p.idx[(int64_t)r * p.topk + e] : -1;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    ent[h] = (pos[h] >= 0 && (uint32_t)pos[h] < cap) ? p.bt[(int64_t)b * p.W + (pos[h] >> p.bshift)] : -1;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = wave + kWaves * h;
+    if (t < ntiles) {
+      const bool pad = pos[h] < 0;
+      const bool ok = !pad && (uint32_t)pos[h] < cap && ent[h] >= 0 && (uint32_t)ent[h] < p.nblk;
+      const int row = ok ? (ent[h] << p.bshift) | (pos[h] & smask) : 0;
+      // Padding and bad positions load the first valid row of the tile (or row 0).
+      const uint64_t okm = __ballot(ok);
+      const uint64_t padm = __ballot(pad);
+      const uint64_t badm = __ballot(!pad && !ok);
+      const int sub = __shfl(row, okm ? __ffsll((unsigned long long)okm) - 1 : 0);
+      sm.rows[t][lane] = ok ? row : sub;
+      if (lane == 0) {
+        sm.padm[t] = padm;
+        sm.badm[t] = badm;
       }
     }
-    // Padding and bad positions load the first valid row of the tile (or row 0).
-    const uint64_t okm = __ballot(st == kValid);
-    const int first = okm ? __ffsll((unsigned long long)okm) - 1 : 0;
-    const int sub = __shfl(row, first);
-    sm.rows[t][lane] = st == kValid ? row : sub;
-    sm.stat[t][lane] = (uint8_t)st;
   }
   __syncthreads();
-  if (wave == 0) {
+  if (threadIdx.x == 0) {  // live tiles: not all padding
     int n = 0;
-    for (int t = 0; t < ntiles; ++t) {
-      const bool any = __ballot(sm.stat[t][lane] != kPad) != 0;
-      if (any) {
-        if (lane == 0) sm.live[n] = t;
-        ++n;
-      }
-    }
-    if (lane == 0) sm.nlive = n;
+    for (int t = 0; t < ntiles; ++t)
+      if (sm.padm[t] != ~0ull) sm.live[n++] = t;
+    sm.nlive = n;
   }
   __syncthreads();
   const int nlive = uniform(sm.nlive);
-  // Compact the live tiles' rows to the front (in place: live[k] >= k).
+  // Compact the live tiles to the front (in place: live[k] >= k).
   int myrow[kMaxTiles];
-  uint8_t mystat[kMaxTiles];
+  uint64_t mypad[kMaxTiles], mybad[kMaxTiles];
 #pragma unroll
   for (int k = 0; k < kMaxTiles; ++k) {
     if (k < nlive) {
       const int t = sm.live[k];
       myrow[k] = sm.rows[t][lane];
-      mystat[k] = sm.stat[t][lane];
+      mypad[k] = sm.padm[t];
+      mybad[k] = sm.badm[t];
     }
   }
   __syncthreads();
@@ -265,7 +270,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
     for (int k = 0; k < kMaxTiles; ++k)
       if (k < nlive) {
         sm.rows[k][lane] = myrow[k];
-        sm.stat[k][lane] = mystat[k];
+        if (lane == 0) {
+          sm.padm[k] = mypad[k];
+          sm.badm[k] = mybad[k];
+        }
       }
   }
   __syncthreads();
@@ -293,23 +301,42 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
     if (k + kNBuf - 1 < nlive) issue_tile(p, sm, k + kNBuf - 1, (k + kNBuf - 1) & (kNBuf - 1), wave, lane);
     const uint8_t* const tb = sm.tile[buf];
 
-    // S^T for tokens 16*wave + (0..15): lane (G, i) reads dims [32s + 8G, +8) of its token.
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint64_t padm = ((uint64_t)(uint32_t)uniform((int)(uint32_t)sm.padm[k])) |
+                          ((uint64_t)(uint32_t)uniform((int)(uint32_t)(sm.padm[k] >> 32)) << 32);
+    const uint64_t badm = ((uint64_t)(uint32_t)uniform((int)(uint32_t)sm.badm[k])) |
+                          ((uint64_t)(uint32_t)uniform((int)(uint32_t)(sm.badm[k] >> 32)) << 32);
+
+    // Every LDS read of the tile first: the key operands of the scores (lane (G, i): dims
+    // [32s + 8G, +8) of token 16*wave + i) and the value operands (transposed reads,
+    // independent of the softmax).
+    i32x2 kx[kD / 32];
     {
       const uint8_t* kr = tb + (16 * wave + i) * kRowStride + 8 * G;
 #pragma unroll
-      for (int s = 0; s < kD / 32; ++s) {
-        const i32x2 x = *reinterpret_cast<const i32x2*>(kr + 32 * s);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8_to_f16(x.x, x.y), qb[s], acc, 0, 0, 0);
-      }
+      for (int s = 0; s < kD / 32; ++s) kx[s] = *reinterpret_cast<const i32x2*>(kr + 32 * s);
     }
+    i32x2 vx[2][8];
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg) {
+      const uint8_t* vr = tb + (32 * sg + 8 * G + (i >> 1)) * kRowStride + 128 * wave + 8 * (i & 1);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+        vx[sg][ct] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vr + 16 * ct));
+    }
+
+    // S^T for tokens 16*wave + (0..15).
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < kD / 32; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8_to_f16(kx[s].x, kx[s].y), qb[s], acc, 0, 0, 0);
     // acc[v]: token 16*wave + 4G + v, head i.
     float sc[4];
     float mx = -__builtin_inff();
+    const int u0 = 16 * wave + 4 * G;
+    const uint32_t padv = (uint32_t)(padm >> u0) & 0xFu, badv = (uint32_t)(badm >> u0) & 0xFu;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int st = sm.stat[k][16 * wave + 4 * G + v];
-      sc[v] = st == kValid ? acc[v] * p.c2 : (st == kPad ? -__builtin_inff() : __builtin_nanf(""));
+      sc[v] = (padv >> v) & 1u ? -__builtin_inff() : ((badv >> v) & 1u ? __builtin_nanf("") : acc[v] * p.c2);
       mx = __builtin_fmaxf(mx, sc[v]);
     }
     mx = groups_max(mx);
@@ -345,26 +372,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) o[ct] *= alpha;
 
-    // Padding bytes of the value operands: token 32*sg + 8G + j is byte j.
-    uint32_t keep_lo[2], keep_hi[2];
-#pragma unroll
-    for (int sg = 0; sg < 2; ++sg) {
-      uint32_t pm = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pm |= (sm.stat[k][32 * sg + 8 * G + j] == kPad ? 1u : 0u) << j;
-      keep_lo[sg] = ~bytes_of_bits(pm);
-      keep_hi[sg] = ~bytes_of_bits(pm >> 4);
-    }
     // O^T[cols, heads] += V^T P^T over the tile's 64 tokens, columns 128*wave + 16*ct.
+    // Value bytes of padding tokens (token 32*sg + 8G + j is byte j) are zeroed.
 #pragma unroll
     for (int sg = 0; sg < 2; ++sg) {
-      const uint8_t* vr = tb + (32 * sg + 8 * G + (i >> 1)) * kRowStride + 128 * wave + 8 * (i & 1);
+      const uint32_t pm = (uint32_t)(padm >> (32 * sg + 8 * G)) & 0xFFu;
+      const uint32_t keep_lo = ~bytes_of_bits(pm), keep_hi = ~bytes_of_bits(pm >> 4);
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
-        i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vr + 16 * ct));
-        x.x &= (int)keep_lo[sg];
-        x.y &= (int)keep_hi[sg];
-        o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8_to_f16(x.x, x.y), pb[sg], o[ct], 0, 0, 0);
+        const int lo = vx[sg][ct].x & (int)keep_lo, hi = vx[sg][ct].y & (int)keep_hi;
+        o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8_to_f16(lo, hi), pb[sg], o[ct], 0, 0, 0);
       }
     }
   }
@@ -390,35 +407,27 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
   }
 }
 
-// Merges the splits' partial states of row blockIdx.x (grid R, 256 threads): per head,
-// M = max of the splits' maxima, weights 2^(m_s - M), out = sum w_s O_s / sum w_s l_s.
-__global__ __launch_bounds__(256) void sparse_mla_combine_kernel(Params p) {
-  const int r = blockIdx.x;
+// Merges the splits' partial states (grid (16 heads, rows), 128 threads, a float4 of
+// columns per thread): M = max of the splits' maxima, weights 2^(m_s - M),
+// out = kv_scale * sum w_s O_s / sum w_s l_s.
+__global__ __launch_bounds__(128) void sparse_mla_combine_kernel(Params p) {
+  const int h = blockIdx.x;
+  const int r = blockIdx.y;
   const float* base = p.ws + (int64_t)r * p.splits * kPartial;
-  // Thread t: head t / 16, columns [32 (t % 16), +32).
-  const int h = threadIdx.x >> 4;
-  const int c0 = 32 * (threadIdx.x & 15);
   float M = -__builtin_inff();
   for (int s = 0; s < p.splits; ++s) M = __builtin_fmaxf(M, base[s * kPartial + kH * kDV + h]);
   const float m_use = M == -__builtin_inff() ? 0.0f : M;
-  f32x4 acc[8];
-#pragma unroll
-  for (int v = 0; v < 8; ++v) acc[v] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float L = 0.0f;
   for (int s = 0; s < p.splits; ++s) {
     const float* part = base + s * kPartial;
-    const float ms = part[kH * kDV + h];
-    const float w = __builtin_amdgcn_exp2f(ms - m_use);  // 0 for a split that saw nothing
+    const float w = __builtin_amdgcn_exp2f(part[kH * kDV + h] - m_use);  // 0 for a split that saw nothing
     L += w * part[kH * kDV + kH + h];
-    const f32x4* src = reinterpret_cast<const f32x4*>(part + h * kDV + c0);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) acc[v] += w * src[v];
+    acc += w * *reinterpret_cast<const f32x4*>(part + h * kDV + 4 * threadIdx.x);
   }
   const float f = L == 0.0f ? 0.0f : p.vscale / L;
-  f32x4* dst = reinterpret_cast<f32x4*>(p.out + ((int64_t)r * kH + h) * kDV + c0);
-#pragma unroll
-  for (int v = 0; v < 8; ++v) dst[v] = acc[v] * f;
-  if (p.lse && (threadIdx.x & 15) == 0)
+  *reinterpret_cast<f32x4*>(p.out + ((int64_t)r * kH + h) * kDV + 4 * threadIdx.x) = acc * f;
+  if (p.lse && threadIdx.x == 0)
     p.lse[(int64_t)r * kH + h] = L > 0.0f ? (M + __builtin_amdgcn_logf(L) - 15.0f) * kLn2 : (L == 0.0f ? -__builtin_inff() : L);
 }
 
@@ -465,7 +474,7 @@ hipError_t launch_sparse_mla(const SparseMlaLaunch& a, const SparseMlaPlan& plan
   p.nblk = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
   hipLaunchKernelGGL(sparse_mla_kernel, dim3((unsigned)plan.splits, (unsigned)a.rows), dim3(kThreads), 0, stream, p);
   if (plan.splits > 1)
-    hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3((unsigned)a.rows), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(kH, (unsigned)a.rows), dim3(kDV / 4), 0, stream, p);
   return hipGetLastError();
 }
 
