@@ -408,22 +408,30 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
 }
 
 // Merges the splits' partial states (grid (16 heads, rows), 128 threads, a float4 of
-// columns per thread): M = max of the splits' maxima, weights 2^(m_s - M),
-// out = kv_scale * sum w_s O_s / sum w_s l_s.
+// columns per thread) in one pass with a running maximum: per split, M' = max(M, m_s),
+// acc = acc * 2^(M - M') + 2^(m_s - M') * O_s, L likewise; out = kv_scale * acc / L.
+// The loads of consecutive splits do not depend on each other, so they are in flight
+// together.
 __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(Params p) {
   const int h = blockIdx.x;
   const int r = blockIdx.y;
   const float* base = p.ws + (int64_t)r * p.splits * kPartial;
   float M = -__builtin_inff();
-  for (int s = 0; s < p.splits; ++s) M = __builtin_fmaxf(M, base[s * kPartial + kH * kDV + h]);
-  const float m_use = M == -__builtin_inff() ? 0.0f : M;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float L = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
   for (int s = 0; s < p.splits; ++s) {
     const float* part = base + s * kPartial;
-    const float w = __builtin_amdgcn_exp2f(part[kH * kDV + h] - m_use);  // 0 for a split that saw nothing
-    L += w * part[kH * kDV + kH + h];
-    acc += w * *reinterpret_cast<const f32x4*>(part + h * kDV + 4 * threadIdx.x);
+    const float ms = part[kH * kDV + h];
+    const float ls = part[kH * kDV + kH + h];
+    const f32x4 os = *reinterpret_cast<const f32x4*>(part + h * kDV + 4 * threadIdx.x);
+    const float mn = __builtin_fmaxf(M, ms);
+    const float mu = mn == -__builtin_inff() ? 0.0f : mn;
+    const float a = __builtin_amdgcn_exp2f(M - mu);   // 0 while nothing has been seen
+    const float w = __builtin_amdgcn_exp2f(ms - mu);  // 0 for a split that saw nothing
+    acc = acc * a + os * w;
+    L = L * a + ls * w;
+    M = mn;
   }
   const float f = L == 0.0f ? 0.0f : p.vscale / L;
   *reinterpret_cast<f32x4*>(p.out + ((int64_t)r * kH + h) * kDV + 4 * threadIdx.x) = acc * f;

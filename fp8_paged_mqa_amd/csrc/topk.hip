@@ -168,7 +168,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Core& sh, i
 __device__ void find_bin(Core& sh, int nbins, uint32_t rem) {
   const int per = nbins / kThreads;  // 2 or 4
   const int top = nbins - 1 - per * (int)threadIdx.x;
-  uint32_t cnt[4] = {0, 0, 0, 0}, sum = 0;
+  uint32_t cnt[kKeyBins / kThreads] = {}, sum = 0;
   for (int i = 0; i < per; ++i) {
     cnt[i] = sh.hist[top - i];
     sum += cnt[i];
