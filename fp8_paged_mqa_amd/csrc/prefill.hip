@@ -21,10 +21,11 @@
 //     added until there are about four workgroups per CU. A workgroup computes the
 //     64-key stages of its split that meet the union of its rows' windows and writes
 //     -inf over the rest of its split (nontemporal stores).
-//   * Stage pipeline: two LDS buffers. While the waves compute stage s from one, every
-//     thread converts its 16 key bytes of stage s+1 (loaded during stage s-1; the
-//     scale's sign folded into the fp8 sign bits, exact) into the other and loads its
-//     bytes of stage s+2. One barrier per stage.
+//   * Stage pipeline: two LDS buffers. At the start of stage s every thread converts its
+//     16 key bytes of stage s+1 (loaded during stage s-1; the scale's sign folded into
+//     the fp8 sign bits, exact) into the other buffer and loads its bytes of stage s+2,
+//     then the waves compute stage s: the conversion and LDS writes overlap the MFMAs.
+//     One barrier per stage.
 //   * LDS layout per 32-key tile: [k-step 0..7][lane 0..63][8 f16], so each k-step's B
 //     operands are one conflict-free 1 KB ds_read_b128 per wave.
 //   * Epilogue: a lane's 16 results are heads 8q + 4h + r (q, r < 4) of key j; relu,
@@ -220,6 +221,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_logits_kernel(Params p) {
   __syncthreads();
   int buf = 0;
   for (int s0 = c0; s0 < c1; s0 += kStage) {
+    // Next stage into the other buffer first (its bytes were loaded a whole stage ago, and
+    // its buffer was last read before the previous barrier), so the conversion and the
+    // LDS writes overlap this stage's MFMAs; then the load two stages ahead.
+    if (s0 + kStage < c1) {
+      stash(buf ^ 1, raw, sc);
+      if (s0 + 2 * kStage < c1) fetch(s0 + 2 * kStage, raw, sc);
+    }
     const uint8_t* const bop = bops[buf];
     const float* const sab = sabs[buf];
     float keep[QPW];
@@ -261,10 +269,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_logits_kernel(Params p) {
 #pragma unroll
       for (int jl = 0; jl < QPW; ++jl)
         if (live[jl]) orow[jl][t] = (t >= lo_r[jl] && t < hi_r[jl]) ? keep[jl] : -__builtin_inff();
-    }
-    if (s0 + kStage < c1) {  // next stage into the other buffer (last read two stages ago)
-      stash(buf ^ 1, raw, sc);
-      if (s0 + 2 * kStage < c1) fetch(s0 + 2 * kStage, raw, sc);
     }
     __syncthreads();
     buf ^= 1;
