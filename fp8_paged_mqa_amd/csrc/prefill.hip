@@ -219,15 +219,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_logits_kernel(Params p) {
   stash(0, raw, sc);
   fetch(min(c0 + kStage, c1 - 1), raw, sc);
   __syncthreads();
+  // A stage's logits are stored one stage later, just before the next key load: the
+  // wait for that load (vector-memory counters also count stores) then finds the stores
+  // long done instead of waiting for them.
+  float held[QPW];
+  int held_t = -1;  // key of this lane in the held stage (-1: nothing held)
+  auto store_held = [&]() {
+    if (held_t >= 0 && held_t < c1) {
+#pragma unroll
+      for (int jl = 0; jl < QPW; ++jl)
+        if (live[jl]) orow[jl][held_t] = (held_t >= lo_r[jl] && held_t < hi_r[jl]) ? held[jl] : -__builtin_inff();
+    }
+  };
   int buf = 0;
   for (int s0 = c0; s0 < c1; s0 += kStage) {
     // Next stage into the other buffer first (its bytes were loaded a whole stage ago, and
     // its buffer was last read before the previous barrier), so the conversion and the
-    // LDS writes overlap this stage's MFMAs; then the load two stages ahead.
-    if (s0 + kStage < c1) {
-      stash(buf ^ 1, raw, sc);
-      if (s0 + 2 * kStage < c1) fetch(s0 + 2 * kStage, raw, sc);
-    }
+    // LDS writes overlap this stage's MFMAs; then the held stores, then the load two
+    // stages ahead.
+    if (s0 + kStage < c1) stash(buf ^ 1, raw, sc);
+    store_held();
+    if (s0 + 2 * kStage < c1) fetch(s0 + 2 * kStage, raw, sc);
     const uint8_t* const bop = bops[buf];
     const float* const sab = sabs[buf];
     float keep[QPW];
@@ -264,15 +276,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_logits_kernel(Params p) {
         if (h == u) keep[jl] = part;
       }
     }
-    const int t = s0 + lane;  // lane (h, j) stores key 32h + j of the stage
-    if (t < c1) {
+    held_t = s0 + lane;  // lane (h, j) stores key 32h + j of the stage
 #pragma unroll
-      for (int jl = 0; jl < QPW; ++jl)
-        if (live[jl]) orow[jl][t] = (t >= lo_r[jl] && t < hi_r[jl]) ? keep[jl] : -__builtin_inff();
-    }
+    for (int jl = 0; jl < QPW; ++jl) held[jl] = keep[jl];
     __syncthreads();
     buf ^= 1;
   }
+  store_held();
 }
 
 using KernelFn = void (*)(Params);
