@@ -1,5 +1,7 @@
 /*
- * mqa.h - C ABI of libmqa: fp8 paged MQA logits and per-row top-k on MI355X (gfx950).
+ * mqa.h - C ABI of libmqa: fp8 paged MQA logits and per-row top-k on MI355X (gfx950),
+ * with the non-paged (prefill) form of the logits, the indexer K-cache write and the
+ * sparse MLA decode over the selected positions.
  *
  * The operation is the decode step of the sparse-attention indexer described on
  * the stepcodex.com issue page "[Bug] aiter ops triton attention pa_mqa_logits"
