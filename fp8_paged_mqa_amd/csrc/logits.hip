@@ -279,6 +279,11 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
       auto load_table = [&](int st) -> int {
         return btb[st < nstage ? min((t0 + st * kStage + lane) >> p.bshift, wmax) : 0];
       };
+      // Table entries of the first two stages first: the gathers wait for them, and a
+      // wait on a load also waits for every load issued before it.
+      int tab0 = load_table(0);
+      int tab1 = load_table(1);
+      __builtin_amdgcn_sched_barrier(0);
       // Query rows of this segment: raw bytes now, f16 A operands once the first key
       // gathers are on their way (the conversion then overlaps their latency).
       i32x4 qraw[TILES][2];
@@ -296,9 +301,6 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
           wv[m] = *reinterpret_cast<const f32x4*>(wb + mr * 16 + 4 * g);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      int tab0 = load_table(0);
-      int tab1 = load_table(1);
       __builtin_amdgcn_sched_barrier(0);
       Operand qa[TILES];
 
