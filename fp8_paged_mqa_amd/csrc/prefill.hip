@@ -30,8 +30,12 @@
 //     operands are one conflict-free 1 KB ds_read_b128 per wave.
 //   * Epilogue: a lane's 16 results are heads 8q + 4h + r (q, r < 4) of key j; relu,
 //     weights and the head sum run in registers, one permlane32 swap adds the two lane
-//     halves, then |scale| and the window mask; a row's 64 logits of a stage leave as
-//     one 256-byte store.
+//     halves, then |scale| and the window mask. Each 32-key group's epilogue runs one
+//     group late, between the next group's MFMAs (the second group's across the stage
+//     barrier), and a stage's 64 logits per row leave as one 256-byte store once its
+//     second group is done. The stores are range-checked buffer stores (keys past the
+//     computed range are dropped by the hardware), so they need no branch and the
+//     compiler's wait counts for the key loads stay exact.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -193,96 +197,125 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_logits_kernel(Params p) {
     }
   }
 
-  // Stage loader: thread t holds bytes [16*(t%8), +16) of key t/8 of the stage, i.e. the
-  // k-steps 2*(t%4), 2*(t%4)+1 of lane (h, j) = ((t%8)/4, key%32) of tile key/32.
+  // Stage loader: piece P = t + kThreads*e of a stage is bytes [16*(P%8), +16) of key P/8,
+  // i.e. the k-steps 2*(P%4), 2*(P%4)+1 of lane (h, j) = ((P%8)/4, key%32) of tile P/256.
+  constexpr int kPieces = kStage * kD / (16 * kThreads);
+  static_assert(kPieces * kThreads * 16 == kStage * kD, "a stage is whole 16-byte pieces");
   const int lk = threadIdx.x >> 3;
   const int lb = (threadIdx.x & 7) * 16;
-  const int dst_off = (lk >> 5) * kTileBytes + ((threadIdx.x & 3) * 2) * 1024 + ((lb >> 6) * 32 + (lk & 31)) * 16;
-  auto fetch = [&](int s0, i32x4& raw, float& sc) {
-    const int key = min(s0 + lk, N - 1);
-    raw = load16(p.k + (int64_t)key * kD + lb);
-    sc = p.ksc[key];
+  const int dst_off = ((threadIdx.x & 3) * 2) * 1024 + ((lb >> 6) * 32 + (lk & 31)) * 16;
+  auto fetch = [&](int s0, i32x4 (&raw)[kPieces], float (&sc)[kPieces]) {
+#pragma unroll
+    for (int e = 0; e < kPieces; ++e) {
+      const int key = min(s0 + lk + (kThreads / 8) * e, N - 1);
+      raw[e] = load16(p.k + (int64_t)key * kD + lb);
+      sc[e] = p.ksc[key];
+    }
   };
-  auto stash = [&](int buf, i32x4 raw, float sc) {
-    if (__float_as_int(sc) < 0) raw ^= (int)0x80808080;  // sign of the scale into the codes
-    *reinterpret_cast<f16x8*>(bops[buf] + dst_off) = fp8x8_to_f16(raw.x, raw.y);
-    *reinterpret_cast<f16x8*>(bops[buf] + dst_off + 1024) = fp8x8_to_f16(raw.z, raw.w);
-    if ((threadIdx.x & 7) == 0) sabs[buf][lk] = __builtin_fabsf(sc);
+  auto stash = [&](int buf, const i32x4 (&raw)[kPieces], const float (&sc)[kPieces]) {
+#pragma unroll
+    for (int e = 0; e < kPieces; ++e) {
+      i32x4 x = raw[e];
+      if (__float_as_int(sc[e]) < 0) x ^= (int)0x80808080;  // sign of the scale into the codes
+      uint8_t* dst = bops[buf] + ((lk + (kThreads / 8) * e) >> 5) * kTileBytes + dst_off;
+      *reinterpret_cast<f16x8*>(dst) = fp8x8_to_f16(x.x, x.y);
+      *reinterpret_cast<f16x8*>(dst + 1024) = fp8x8_to_f16(x.z, x.w);
+      if ((threadIdx.x & 7) == 0) sabs[buf][lk + (kThreads / 8) * e] = __builtin_fabsf(sc[e]);
+    }
   };
 
-  // Double-buffered stages: stage s is computed from one LDS buffer while stage s+1,
-  // loaded into registers during stage s-1, is converted into the other; one barrier
-  // per stage. Key bytes run two stages ahead of their use.
-  i32x4 raw;
-  float sc;
+  // Output rows as range-checked buffer resources: a lane's store of key t lands only if
+  // t < c1 (and the row exists), without a branch, so the compiler's wait counts for the
+  // key loads stay exact instead of falling back to waiting for every store.
+  __amdgpu_buffer_rsrc_t orsrc[QPW];
+#pragma unroll
+  for (int jl = 0; jl < QPW; ++jl)
+    orsrc[jl] = __builtin_amdgcn_make_buffer_rsrc(orow[jl], 0, live[jl] ? c1 * 4 : 0, 0x00020000);
+
+  // Per 32-key tile group u of a stage: MFMAs into one accumulator set, then the epilogue
+  // (relu, weights, head sum, |scale|) one group later, so the VALU work of group g runs
+  // between the MFMAs of group g+1 - across the stage barrier for the second group, whose
+  // epilogue runs during the next stage's first group. Lane (h, j) keeps key 32h + j of
+  // a stage (from group h); a stage's logits are stored once its second group is done.
+  float keep[QPW];
+#pragma unroll
+  for (int jl = 0; jl < QPW; ++jl) keep[jl] = 0.0f;
+  auto epilogue = [&](const f32x16 (&acc)[TILES], float s, int u) {
+#pragma unroll
+    for (int jl = 0; jl < QPW; ++jl) {
+      float part = 0.0f;
+#pragma unroll
+      for (int mm = 0; mm < T32; ++mm) {
+        const int t = jl * T32 + mm;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          part = __builtin_fmaf(wv[t][v / 4][v % 4], __builtin_elementwise_maximum(acc[t][v], 0.0f), part);
+      }
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+      part = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * s;  // both halves: key 32u + j
+      if (h == u) keep[jl] = part;
+    }
+  };
+  auto store_stage = [&](int base) {
+    const int t = base + lane;
+#pragma unroll
+    for (int jl = 0; jl < QPW; ++jl) {
+      const float v = (t >= lo_r[jl] && t < hi_r[jl]) ? keep[jl] : -__builtin_inff();
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc[jl], t * 4, 0, 0);  // the bits
+    }
+  };
+
+  // Double-buffered stages: at the start of stage s every thread converts its key pieces
+  // of stage s+1 (loaded during stage s-1) into the other buffer and loads those of stage
+  // s+2; one barrier per stage.
+  i32x4 raw[kPieces];
+  float sc[kPieces];
   fetch(c0, raw, sc);
   stash(0, raw, sc);
   fetch(min(c0 + kStage, c1 - 1), raw, sc);
   __syncthreads();
-  // A stage's logits are stored one stage later, just before the next key load: the
-  // wait for that load (vector-memory counters also count stores) then finds the stores
-  // long done instead of waiting for them.
-  float held[QPW];
-  int held_t = -1;  // key of this lane in the held stage (-1: nothing held)
-  auto store_held = [&]() {
-    if (held_t >= 0 && held_t < c1) {
-#pragma unroll
-      for (int jl = 0; jl < QPW; ++jl)
-        if (live[jl]) orow[jl][held_t] = (held_t >= lo_r[jl] && held_t < hi_r[jl]) ? held[jl] : -__builtin_inff();
-    }
-  };
+  f32x16 accP[TILES];  // the group whose epilogue is pending
+  float sP = 0.0f;
+  int uP = -1;         // its group index (-1: none pending)
+  int baseP = 0;       // first key of its stage
   int buf = 0;
   for (int s0 = c0; s0 < c1; s0 += kStage) {
-    // Next stage into the other buffer first (its bytes were loaded a whole stage ago, and
-    // its buffer was last read before the previous barrier), so the conversion and the
-    // LDS writes overlap this stage's MFMAs; then the held stores, then the load two
-    // stages ahead.
     if (s0 + kStage < c1) stash(buf ^ 1, raw, sc);
-    store_held();
     if (s0 + 2 * kStage < c1) fetch(s0 + 2 * kStage, raw, sc);
     const uint8_t* const bop = bops[buf];
-    const float* const sab = sabs[buf];
-    float keep[QPW];
-#pragma unroll
-    for (int jl = 0; jl < QPW; ++jl) keep[jl] = 0.0f;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {  // two 32-key tiles per stage
       Operand8 kb;
 #pragma unroll
       for (int st = 0; st < 8; ++st)
         kb.k[st] = *reinterpret_cast<const f16x8*>(bop + u * kTileBytes + st * 1024 + lane * 16);
-      f32x16 acc[TILES];
+      f32x16 accC[TILES];
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t].k[0], kb.k[0], f32x16{}, 0, 0, 0);
+        accC[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t].k[0], kb.k[0], f32x16{}, 0, 0, 0);
 #pragma unroll
       for (int st = 1; st < 8; ++st)
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t].k[st], kb.k[st], acc[t], 0, 0, 0);
-      const float s = sab[u * 32 + j];
-#pragma unroll
-      for (int jl = 0; jl < QPW; ++jl) {
-        float part = 0.0f;
-#pragma unroll
-        for (int mm = 0; mm < T32; ++mm) {
-          const int t = jl * T32 + mm;
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            part = __builtin_fmaf(wv[t][v / 4][v % 4], __builtin_elementwise_maximum(acc[t][v], 0.0f), part);
-        }
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-        part = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * s;  // both halves: key 32u + j
-        if (h == u) keep[jl] = part;
+          accC[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t].k[st], kb.k[st], accC[t], 0, 0, 0);
+      const float sC = sabs[buf][u * 32 + j];
+      if (uP >= 0) {  // uniform
+        epilogue(accP, sP, uP);
+        if (uP == 1) store_stage(baseP);
       }
-    }
-    held_t = s0 + lane;  // lane (h, j) stores key 32h + j of the stage
 #pragma unroll
-    for (int jl = 0; jl < QPW; ++jl) held[jl] = keep[jl];
+      for (int t = 0; t < TILES; ++t) accP[t] = accC[t];
+      sP = sC;
+      uP = u;
+      baseP = s0;
+    }
     __syncthreads();
     buf ^= 1;
   }
-  store_held();
+  if (uP >= 0) {
+    epilogue(accP, sP, uP);
+    store_stage(baseP);
+  }
 }
 
 using KernelFn = void (*)(Params);
