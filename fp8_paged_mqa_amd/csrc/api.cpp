@@ -70,7 +70,7 @@ const char* mqa_status_string(int status) {
       return "unsupported: needs head_dim 128, block_size a power of two up to 65536 (with "
              "block_table_stride * block_size and, for block_size > 1, num_blocks * block_size "
              "below 2^31), heads a multiple of 16 up to 128, "
-             "next_n 1..4, max_model_len <= 2^30, batch <= 8192 for the logits, k 1..2048, 16-byte aligned q and weights, "
+             "next_n 1..4, max_model_len <= 2^30, batch <= 8192 for the logits, k 1..2048, non-paged n <= 2^29, 16-byte aligned q and weights, "
              "4-byte aligned kv_cache, logits, idx and integer arrays; sparse MLA decode: heads 16, "
              "head_dim 576, v_dim 512, rows <= 65535, topk <= 2^20, 16-byte aligned q, kv_cache, out and workspace";
     case MQA_ERR_WORKSPACE: return "workspace missing or too small";
@@ -144,6 +144,7 @@ int mqa_logits(const uint8_t* q, const uint8_t* k, const float* k_scale, const f
                int32_t heads, hipStream_t stream) {
   if (m < 0 || n < 1 || heads < 1 || out_stride < n) return MQA_ERR_SHAPE;
   if (heads % 16 != 0 || heads > 64) return MQA_ERR_UNSUPPORTED;
+  if (n > (1 << 29)) return MQA_ERR_UNSUPPORTED;  // byte offsets of a row stay below 2^31
   if (m == 0) return MQA_OK;
   if (!q || !k || !k_scale || !weights || !ks || !ke || !out) return MQA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(weights, 16) || !aligned(k_scale, 4) || !aligned(ks, 4) ||

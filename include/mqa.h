@@ -154,7 +154,7 @@ int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model
  *   ks, ke      int32 [m]
  *   out         float [m, out_stride], out_stride >= n; elements [n, out_stride) of a row
  *               are not touched
- *   m >= 0 (0 enqueues nothing), n >= 1, heads a multiple of 16 in [16, 64]
+ *   m >= 0 (0 enqueues nothing), 1 <= n <= 2^29, heads a multiple of 16 in [16, 64]
  * Accuracy as mqa_paged_logits (exact fp8 products, fp32 accumulation).
  * Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED or MQA_ERR_HIP.
  */

@@ -168,6 +168,7 @@ def call_prefill(m=4, n=64, heads=32, stride=64, ptrs=(FAKE,) * 7):
     (dict(stride=63), mqa.MQA_ERR_SHAPE),
     (dict(heads=24), mqa.MQA_ERR_UNSUPPORTED),
     (dict(heads=80), mqa.MQA_ERR_UNSUPPORTED),
+    (dict(n=(1 << 29) + 1, stride=(1 << 29) + 1), mqa.MQA_ERR_UNSUPPORTED),
     (dict(ptrs=(None,) + (FAKE,) * 6), mqa.MQA_ERR_NULL),
     (dict(ptrs=(FAKE,) * 6 + (None,)), mqa.MQA_ERR_NULL),
     (dict(ptrs=(ctypes.c_void_p(0x10008),) + (FAKE,) * 6), mqa.MQA_ERR_UNSUPPORTED),
