@@ -55,6 +55,8 @@
 //     stores: nothing reads it back soon, and the write rate rises from ~4.0 to ~5.5 TB/s.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "launch.h"
 
 namespace mqa {
@@ -509,7 +511,15 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, lds) !=
           hipSuccess || per_cu < 1)
     per_cu = 1;
-  const int blocks = compute_units() * per_cu;
+  // One round of persistent workgroups, but no more waves than there can be work for:
+  // the host knows an upper bound of the key stages (every request at its largest
+  // context) and of the tail chunks, and small calls then launch a small grid.
+  const int64_t ctx_cap = a.max_model_len < (int64_t)p.Wt ? a.max_model_len : (int64_t)p.Wt;
+  const int64_t stage_bound = (int64_t)a.batch * ((ctx_cap + kStage - 1) / kStage) * p.groups;
+  const int64_t tail_bound = (int64_t)a.batch * a.next_n * ((a.max_model_len + kTailChunk - 1) / kTailChunk);
+  const int64_t need = (std::max(stage_bound, tail_bound) + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t full = (int64_t)compute_units() * per_cu;
+  const int blocks = (int)std::max<int64_t>(1, std::min(full, need));
   hipLaunchKernelGGL(fn, dim3(blocks), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
