@@ -1,6 +1,6 @@
 """Throughput of the fp8 paged MQA indexer (logits + top-2048) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 1..5] [--block-size S] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--block-size S] [--no-cpu-baseline]
     python bench.py --op kwrite [--tokens T]   (the K-cache write alone; not the default line)
     python bench.py --op prefill [--m M --n N --heads H]   (non-paged logits; not the default line)
     python bench.py --op mla   (sparse MLA decode over the selected positions; not the default line)
@@ -268,7 +268,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", default=None,
+                    help="named decode workload for the indexer step (default decode_b64_ctx8192)")
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--block-size", type=int, default=1,
                     help="tokens per KV block (1: the pages' layout; the default line uses 1)")
@@ -299,7 +300,8 @@ def main():
     sys.path.insert(0, ROOT)
     from fp8_paged_mqa_amd import mqa, workloads
 
-    w = workloads.make_config(args.config, poison_unused=False, block_size=args.block_size)
+    w = workloads.make_named(args.workload or workloads.DEFAULT_WORKLOAD, poison_unused=False,
+                             block_size=args.block_size)
     print(f"[bench] {w.name}: sum_ctx={w.sum_ctx} pool={w.num_blocks}", file=sys.stderr, flush=True)
     dev = "cuda"
     shape = mqa.make_shape(w.batch, w.next_n, w.heads, w.num_blocks, w.block_tables.shape[1],
@@ -394,7 +396,7 @@ def main():
 
     bytes_logits, bytes_topk = algorithmic_bytes(w)
     achieved = bytes_logits / (t_logits * 1e-6) / 1e9
-    tag = f"config{args.config}" + (f"_bs{w.block_size}" if w.block_size > 1 else "")
+    tag = w.name.split(":")[0] + (f"_bs{w.block_size}" if w.block_size > 1 else "")
     traffic = traffic_from_profile("logits", tag, source_digest(LOGITS_SRC))
     value = w.sum_ctx / (ms_per_step * 1e-3)
     step_gbps = (bytes_logits + bytes_topk) / (ms_per_step * 1e-3) / 1e9

@@ -206,26 +206,31 @@ def _build_blocked(name, rng, *, batch, next_n, heads, ctx, max_model_len, pool,
 
 
 # ---------------------------------------------------------------------------
-# The five named workloads.
+# The five named workloads, keyed by a short name that says what each one is.
 # ---------------------------------------------------------------------------
-CONFIG_NAMES = {
-    1: "decode bs=1 N=1 H=32 ctx=2049 L=4096 identity table (reproducer shape)",
-    2: "decode bs=64 N=1 H=64 ctx~U[1,8192] L=8192 permuted 600k-row pool",
-    3: "MTP verify bs=32 N=2 H=64 ctx~U[2048,32768] L=32768 permuted pool",
-    4: "long context bs=4 N=1 H=64 ctx={65536,131071,131072,202752} L=202752 540k pool, 1% x8 keys",
-    5: "mixed serving bs=128 N=4 H=32 ctx~lognormal(6000,1.2) L=202752 interleaved pool",
+WORKLOADS = {
+    "decode_b1_ctx2049": "decode bs=1 N=1 H=32 ctx=2049 L=4096 identity table (reproducer shape)",
+    "decode_b64_ctx8192": "decode bs=64 N=1 H=64 ctx~U[1,8192] L=8192 permuted 600k-row pool",
+    "mtp_b32_n2_ctx32k": "MTP verify bs=32 N=2 H=64 ctx~U[2048,32768] L=32768 permuted pool",
+    "long_b4_ctx202752": "long context bs=4 N=1 H=64 ctx={65536,131071,131072,202752} L=202752 540k pool, 1% x8 keys",
+    "mixed_b128_n4": "mixed serving bs=128 N=4 H=32 ctx~lognormal(6000,1.2) L=202752 interleaved pool",
 }
+DEFAULT_WORKLOAD = "decode_b64_ctx8192"
 
 
-def make_config(n: int, *, poison_unused: bool = True, seed: int | None = None,
-                block_size: int = 1) -> Workload:
-    """The named workload n. With block_size S > 1 the same context lengths are laid
-    out in blocks of S tokens: the pool becomes ceil(rows / S) blocks (at least the
-    blocks in use) and the table kind is kept; keys and scales are drawn afresh."""
+def make_named(workload: str, *, poison_unused: bool = True, seed: int | None = None,
+               block_size: int = 1) -> Workload:
+    """The named workload (a key of WORKLOADS). With block_size S > 1 the same context
+    lengths are laid out in blocks of S tokens: the pool becomes ceil(rows / S) blocks
+    (at least the blocks in use) and the table kind is kept; keys and scales are drawn
+    afresh."""
+    if workload not in WORKLOADS:
+        raise ValueError(f"unknown workload {workload!r}; one of {list(WORKLOADS)}")
+    n = list(WORKLOADS).index(workload) + 1  # selects the recipe below and the default seed
     rng = np.random.Generator(np.random.PCG64(42 + (n - 1) if seed is None else seed))
-    name = f"config{n}: {CONFIG_NAMES[n]}"
+    name = f"{workload}: {WORKLOADS[workload]}"
     if block_size > 1:
-        return _make_config_blocked(n, rng, name, poison_unused, int(block_size))
+        return _make_named_blocked(n, rng, name, poison_unused, int(block_size))
     if n == 1:
         ctx = np.array([2049])
         return build(name, rng, batch=1, next_n=1, heads=32, ctx=ctx, max_model_len=4096,
@@ -255,8 +260,8 @@ def make_config(n: int, *, poison_unused: bool = True, seed: int | None = None,
     raise ValueError(n)
 
 
-def _make_config_blocked(n, rng, name, poison_unused, bs) -> Workload:
-    # Same context-length draws as make_config's block_size 1 path.
+def _make_named_blocked(n, rng, name, poison_unused, bs) -> Workload:
+    # Same context-length draws as make_named's block_size 1 path.
     if n == 1:
         ctx, kw = np.array([2049]), dict(batch=1, next_n=1, heads=32, max_model_len=4096, rows=2065,
                                          table="identity")

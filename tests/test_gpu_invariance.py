@@ -44,7 +44,7 @@ def test_batch_composition_and_length_bitwise():
 
 
 def test_repeatable():
-    case = wl.make_config(3)
+    case = wl.make_named("mtp_b32_n2_ctx32k")
     g1, i1 = run_gpu(case)
     g2, i2 = run_gpu(case)
     assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32))

@@ -95,10 +95,10 @@ def test_boundary_sweep_large(next_n, heads):
     _parity(case, what=f"sweep>=16383 N={next_n} H={heads}")
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
-def test_named_workload(n):
-    case = wl.make_config(n)
-    _parity(case, what=f"config{n}")
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_named_workload(name):
+    case = wl.make_named(name)
+    _parity(case, what=name)
 
 
 @pytest.mark.parametrize("heads,next_n", [(16, 1), (48, 3), (80, 1), (96, 2), (112, 1), (128, 4)])
