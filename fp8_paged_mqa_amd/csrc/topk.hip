@@ -17,11 +17,17 @@
 //            thread in registers. A block min/max reduction sets 2048 first-level bins
 //            linear in the value (monotone, so bins are ordered like the logits; rows
 //            holding a non-finite value use the top 12 key bits instead). An LDS
-//            histogram and a block scan from the top find the bin holding the k-th
-//            element; everything above it is emitted at offsets from one block scan,
-//            and the threshold bin's elements go to an LDS candidate list. A small list
-//            is finished by counting, for each candidate, the candidates above it; a
-//            large one by further 11-bit radix digits of e.
+//            histogram and a scan from the top find the bin holding the k-th element
+//            (every wave finishes the search itself after one barrier); everything
+//            above it goes to an LDS output list at slots from one atomic per wave and
+//            the lanes' ranks in the wave's mask, and the threshold bin's elements go
+//            to an LDS candidate list the same way. A small list is finished by
+//            counting, for each candidate, the candidates above it; a large one by
+//            further 11-bit radix digits of e. The output list is then written to the
+//            row in one coalesced pass. One CU per row runs this, so its time is set by
+//            the instructions each wave issues: the path keeps per-element work to a
+//            few vector instructions (buffer loads clamped onto the last visible
+//            element, lane masks from one compare each).
 //   long     nv > 8192: 8192-element chunks. A schedule kernel lists the long rows and
 //            their chunks and clears their histograms; persistent kernels then add each
 //            chunk's 12-bit key histogram into the row's global histogram, emit each
@@ -98,6 +104,13 @@ struct Core {
 
 struct Full : Core {
   uint64_t cand[kCap];
+};
+
+// A short row's selected positions are gathered here (LDS slots in any order) and
+// written to the output row in one coalesced pass at the end: scattered 4-byte global
+// stores from every lane cost more than the LDS round trip.
+struct Rows : Full {
+  int32_t sel[kChunk + 64];  // + one dummy slot per lane
 };
 
 // Wave-aggregated append to an LDS counter. Must be called by all 64 lanes of a wave.
@@ -224,6 +237,7 @@ __device__ void rank_select(Full& sh, int n, uint32_t rem, int32_t* out, int k) 
   for (int i = threadIdx.x; i < n; i += kThreads) {
     const uint64_t e = sh.cand[i];
     uint32_t rank = 0;
+#pragma unroll 8
     for (int j = 0; j < n; ++j) rank += sh.cand[j] > e ? 1u : 0u;
     if (rank < rem) {
       const uint32_t slot = atomicAdd(&sh.n_out, 1u);
@@ -296,108 +310,220 @@ __device__ void select_trivial_row(const Params& p, int r, int nv) {
   for (int i = threadIdx.x; i < p.k; i += kThreads) out[i] = i < nv ? i : -1;
 }
 
-// Rows with k < nv <= kChunk: the whole select by one workgroup.
-__device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
+// Sum over lanes 0..15 of a wave of v (min or max for the float forms): row-0 DPP
+// shifts, lane 15 ends with the result, which is returned to every lane.
+__device__ __forceinline__ uint32_t row16_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  return v;
+}
+
+template <bool Max>
+__device__ __forceinline__ float row16_minmax(float v) {
+  v = minmax_step<Max, 0x111, 0xf>(v);
+  v = minmax_step<Max, 0x112, 0xf>(v);
+  v = minmax_step<Max, 0x114, 0xf>(v);
+  v = minmax_step<Max, 0x118, 0xf>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+}
+
+// The threshold bin of a block histogram of nbins = PER * kThreads bins: the bin B with
+// above(B) < rem <= above(B) + hist[B], counting from the top bin, for rem <= the total.
+// Thread t owns bins [nbins - PER*(t+1), nbins - PER*t). Each wave scans its own bins and
+// publishes its total; after one barrier every wave finds the owning wave from the
+// totals, rescans that wave's bins from LDS and so knows B, above(B) and hist[B]
+// without a second barrier. Uses the kRedBin scratch slots.
+template <int PER>
+__device__ __forceinline__ void threshold_bin(Core& sh, uint32_t rem, uint32_t& bin, uint32_t& above,
+                                              uint32_t& count) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int nbins = PER * kThreads;
+  auto lane_bins = [&](int w, uint32_t (&c)[PER]) {
+    const int lo = nbins - PER * (w * 64 + lane + 1);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) c[j] = sh.hist[lo + j];
+  };
+  uint32_t c[PER];
+  lane_bins(wave, c);
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) sum += c[j];
+  const uint32_t incl = wave_scan_add(sum);
+  if (lane == 63) sh.red[kRedBin + wave] = incl;
+  __syncthreads();
+  // Wave totals in lanes 0..15; the owner is the first wave whose inclusive prefix
+  // reaches rem.
+  const uint32_t wt = lane < kWaves ? sh.red[kRedBin + lane] : 0u;
+  uint32_t wi = wt;
+  wi += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wi, 0x111, 0xf, 0xf, false);
+  wi += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wi, 0x112, 0xf, 0xf, false);
+  wi += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wi, 0x114, 0xf, 0xf, false);
+  wi += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wi, 0x118, 0xf, 0xf, false);
+  const uint64_t reach = __ballot(lane < kWaves && wi >= rem);
+  const int ow = __builtin_ctzll(reach);  // rem <= total: some wave reaches it
+  const uint32_t ow_before = (uint32_t)__builtin_amdgcn_readlane((int)(wi - wt), ow);
+  // Rescan the owner's bins (the owner's own registers would do; every wave reads LDS).
+  uint32_t oc[PER];
+  lane_bins(ow, oc);
+  uint32_t osum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) osum += oc[j];
+  const uint32_t oincl = ow_before + wave_scan_add(osum);
+  const uint64_t lreach = __ballot(oincl >= rem);
+  const int ol = __builtin_ctzll(lreach);
+  uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)(oincl - osum), ol);
+  // Walk lane ol's bins from its top bin down.
+  const int olo = nbins - PER * (ow * 64 + ol + 1);
+  bin = 0;
+  above = 0;
+  count = 0;
+  bool found = false;
+#pragma unroll
+  for (int j = PER - 1; j >= 0; --j) {
+    const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)oc[j], ol);
+    const bool hit = !found && rem <= run + cj;
+    bin = hit ? (uint32_t)(olo + j) : bin;
+    above = hit ? run : above;
+    count = hit ? cj : count;
+    found = found || hit;
+    run += cj;
+  }
+}
+
+// Rows with k < nv <= kChunk: the whole select by one workgroup. Element i*kThreads + t
+// of the row sits in thread t's register i. Loads past nv are clamped onto the last
+// visible element, which leaves min, max and finiteness unchanged; histogram and emit
+// count only the elements below nv.
+__device__ void select_short_row(const Params& p, int r, int nv, Rows& sh) {
   const int k = p.k;
   const float* row = p.logits + (int64_t)r * p.L;
   int32_t* out = p.idx + (int64_t)r * k;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, nv * 4, 0x00020000);
+  const uint32_t last = (uint32_t)(nv - 1) * 4u;
   float v[kPer];
-  load_chunk(row, 0, nv, v);
-  for (int i = threadIdx.x; i < kKeyBins; i += kThreads) sh.hist[i] = 0;
-  // Min / max of the visible values; any non-finite value switches to key bins.
-  float lo = __builtin_inff(), hi = -__builtin_inff();
-  bool bad = false;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    if (i * kThreads + (int)threadIdx.x < nv) {
-      if (__builtin_isfinite(v[i])) {
-        lo = fminf(lo, v[i]);
-        hi = fmaxf(hi, v[i]);
-      } else {
-        bad = true;
-      }
-    }
+    const uint32_t off = min((uint32_t)threadIdx.x * 4u + (uint32_t)(i * kThreads * 4), last);
+    v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+  }
+  for (int i = threadIdx.x; i < kKeyBins; i += kThreads) sh.hist[i] = 0;
+  if (threadIdx.x == 0) {  // emit counters; the first use is several barriers later
+    sh.n_out = 0;
+    sh.n_cand = 0;
+  }
+  // Min / max of the visible values; a non-finite value anywhere switches to key bins
+  // (the wave reports it as an infinite maximum).
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  uint64_t bad = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    lo = fminf(lo, v[i]);
+    hi = fmaxf(hi, v[i]);
+    bad |= __ballot(!__builtin_isfinite(v[i]));
   }
   lo = wave_scan_minmax<false>(lo);
   hi = wave_scan_minmax<true>(hi);
-  const bool wave_bad = __ballot(bad) != 0;
   if (lane == 63) {
     sh.red[kRedLo + wave] = __float_as_uint(lo);
-    sh.red[kRedHi + wave] = __float_as_uint(hi);
-    sh.red[kRedBad + wave] = wave_bad ? 1u : 0u;
+    sh.red[kRedHi + wave] = __float_as_uint(bad ? __builtin_inff() : hi);
   }
   __syncthreads();
-  bool nonfinite = false;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    lo = fminf(lo, __uint_as_float(sh.red[kRedLo + w]));
-    hi = fmaxf(hi, __uint_as_float(sh.red[kRedHi + w]));
-    nonfinite |= sh.red[kRedBad + w] != 0;
-  }
+  lo = row16_minmax<false>(__uint_as_float(lane < kWaves ? sh.red[kRedLo + lane] : 0x7f800000u));
+  hi = row16_minmax<true>(__uint_as_float(lane < kWaves ? sh.red[kRedHi + lane] : 0xff800000u));
+  const bool nonfinite = !__builtin_isfinite(hi);
   // Binning: linear in the value when the visible values are finite and spread; by the
   // top key bits when some value is not finite (or the spread is not representable);
   // a single bin when all values are equal (then the refinement starts at bit 64).
+  // Every form is monotone in the value, so bins are ordered like the logits.
   const float spread = hi - lo;
   const float scale = kLinBins / spread;
   const bool linear = !nonfinite && hi > lo && __builtin_isfinite(spread) && __builtin_isfinite(scale) && scale > 0.0f;
   const bool keyed = !linear && (nonfinite || hi > lo);
-  const int nbins = keyed ? kKeyBins : kLinBins;
-  uint32_t key[kPer], bin[kPer];
+  const int tid = (int)threadIdx.x;
+  uint64_t inm[kPer];  // lanes whose element i is below nv
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    key[i] = order_key(v[i]);
-    bin[i] = linear ? (uint32_t)min(kLinBins - 1, (int)((v[i] - lo) * scale))
-                    : (keyed ? key[i] >> (32 - kKeyBits) : 0u);
-    if (i * kThreads + (int)threadIdx.x < nv) atomicAdd(&sh.hist[bin[i]], 1u);
+  for (int i = 0; i < kPer; ++i) inm[i] = __ballot(tid < nv - i * kThreads);
+  uint32_t bin[kPer];
+  if (linear) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) bin[i] = min((uint32_t)(kLinBins - 1), (uint32_t)((v[i] - lo) * scale));
+  } else if (keyed) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) bin[i] = order_key(v[i]) >> (32 - kKeyBits);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) bin[i] = 0u;
   }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (__builtin_amdgcn_inverse_ballot_w64(inm[i])) atomicAdd(&sh.hist[bin[i]], 1u);
   __syncthreads();
-  find_bin(sh, nbins, (uint32_t)k);
-  const uint32_t bin0 = sh.bin;
-  const uint32_t rem = (uint32_t)k - sh.above;
-  const uint32_t cnt0 = sh.hist[bin0];
+  uint32_t bin0, above, cnt0;
+  if (keyed)
+    threshold_bin<kKeyBins / kThreads>(sh, (uint32_t)k, bin0, above, cnt0);
+  else
+    threshold_bin<kLinBins / kThreads>(sh, (uint32_t)k, bin0, above, cnt0);
+  const uint32_t rem = (uint32_t)k - above;
   const bool whole = cnt0 == rem;
-  // Emit the elements above the threshold bin (slots from 0), collect the bin's
-  // elements into the LDS candidate list (slots from 0).
+  // Emit the elements above the threshold bin (the whole bin too when it is all taken)
+  // and collect the bin's own elements into the candidate list. Slots come from one LDS
+  // atomic per wave and counter plus the lane's rank in the wave's mask; lanes that emit
+  // nothing write a private dummy slot. above(bin0) < k and the bin holds at most
+  // nv <= kCap elements, so every slot is in range.
+  const uint32_t thr = whole ? bin0 : bin0 + 1;
+  uint64_t ma[kPer];
   uint32_t na = 0, nb = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const bool in = i * kThreads + (int)threadIdx.x < nv;
-    na += (in && (bin[i] > bin0 || (whole && bin[i] == bin0))) ? 1u : 0u;
-    nb += (in && !whole && bin[i] == bin0) ? 1u : 0u;
+    ma[i] = __ballot(bin[i] >= thr) & inm[i];
+    na += (uint32_t)__popcll(ma[i]);
+    nb += whole ? 0u : (uint32_t)__popcll(__ballot(bin[i] == bin0) & inm[i]);
   }
-  uint32_t total;
-  const uint32_t excl = block_exclusive_scan((na << 16) | nb, sh, kRedEmit, total);
-  uint32_t oa = excl >> 16, ob = excl & 0xFFFFu;
+  uint32_t oa = 0, ob = 0;
+  if (lane == 0) {
+    oa = atomicAdd(&sh.n_out, na);
+    if (nb) ob = atomicAdd(&sh.n_cand, nb);
+  }
+  oa = __builtin_amdgcn_readfirstlane(oa);
+  ob = __builtin_amdgcn_readfirstlane(ob);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int t = i * kThreads + (int)threadIdx.x;
-    const bool in = t < nv;
-    if (in && (bin[i] > bin0 || (whole && bin[i] == bin0))) {
-      if (oa < (uint32_t)k) out[oa] = t;
-      ++oa;
-    } else if (in && !whole && bin[i] == bin0) {
-      if (ob < (uint32_t)kCap) sh.cand[ob] = compose(key[i], t);
-      ++ob;
+    const int t = i * kThreads + tid;
+    const uint32_t ra = __builtin_amdgcn_mbcnt_hi((uint32_t)(ma[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma[i], oa));
+    sh.sel[__builtin_amdgcn_inverse_ballot_w64(ma[i]) ? ra : (uint32_t)(kChunk + lane)] = t;
+    oa += (uint32_t)__popcll(ma[i]);
+    if (nb) {  // the threshold bin's elements (few)
+      const uint64_t mb = __ballot(bin[i] == bin0) & inm[i];
+      if (mb) {
+        const uint32_t rb = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, ob));
+        if (__builtin_amdgcn_inverse_ballot_w64(mb)) sh.cand[rb] = compose(order_key(v[i]), t);
+        ob += (uint32_t)__popcll(mb);
+      }
     }
   }
-  if (threadIdx.x == 0) sh.n_out = total >> 16;
   __syncthreads();
   if (!whole) {
     // Key bins fix the top 12 bits of e; linear or single bins fix none.
     const uint64_t prefix = keyed ? (uint64_t)bin0 << (64 - kKeyBits) : 0ull;
     const uint64_t pmask = keyed ? (uint64_t)(kKeyBins - 1) << (64 - kKeyBits) : 0ull;
-    finish_candidates(sh, (int)cnt0, prefix, pmask, keyed ? 64 - kKeyBits : 64, rem, out, k);
+    finish_candidates(sh, (int)cnt0, prefix, pmask, keyed ? 64 - kKeyBits : 64, rem, sh.sel, k);
   }
+  // k < nv: exactly k slots were filled, and both branches above end at a barrier.
+  for (int i = threadIdx.x; i < k; i += kThreads) out[i] = sh.sel[i];
 }
 
 // Pass 1. Implicit mode (no workspace): workgroup r handles row r. Scheduled mode:
 // persistent workgroups walk long-row chunks (histograms), then short rows, then
 // trivial rows.
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
-  __shared__ Full sh;
+  __shared__ Rows sh;
   if (p.meta == nullptr) {
     const int r = blockIdx.x;
     const int nv = visible(p, r);

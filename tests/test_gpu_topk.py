@@ -1,0 +1,111 @@
+"""mqa_topk on crafted logit rows, one call per path (every row fits one workgroup when
+max_model_len <= 8192; longer rows take the chunked path), compared as sets with the
+oracle's selection (larger first, ties by lower position, -0.0 equal to +0.0).
+
+The rows are chosen to reach each branch of the selection: spread values (linear bins),
+few distinct values (a threshold bin of thousands of elements, refined by radix digits;
+beyond 8192 elements the long path refines from the row itself), a constant row (a single
+bin), signed zeros, infinities and a spread that overflows (top-key bins), a narrow
+band around 1e6, a log-uniform spread over 60 decades, subnormals, and rows holding
+NaNs. The oracle orders NaN below everything; the header fixes the kernel's order for
+NaN as that of the bit patterns (positive NaN above +inf, negative NaN below -inf),
+so NaN rows are checked against that order instead.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_paged_mqa_amd import mqa
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ["normal", "few", "const", "zeros", "inf", "overflow", "narrow", "wide", "subnormal", "nan"]
+
+
+def crafted_row(kind, n, rng):
+    if kind == "normal":
+        return rng.standard_normal(n).astype(np.float32)
+    if kind == "few":
+        return rng.integers(0, 4, n).astype(np.float32)
+    if kind == "const":
+        return np.full(n, 2.5, np.float32)
+    if kind == "zeros":
+        return rng.choice(np.array([-0.0, 0.0, -1.0, 1.0], np.float32), n, p=[0.45, 0.45, 0.05, 0.05])
+    if kind == "inf":
+        x = rng.standard_normal(n).astype(np.float32)
+        x[rng.random(n) < 0.01] = np.inf
+        x[rng.random(n) < 0.01] = -np.inf
+        return x
+    if kind == "overflow":
+        return (rng.uniform(-1.0, 1.0, n) * 3e38).astype(np.float32)
+    if kind == "narrow":
+        return (np.float32(1e6) + rng.integers(0, 64, n).astype(np.float32) * np.float32(0.0625)).astype(np.float32)
+    if kind == "wide":
+        return (rng.choice([-1.0, 1.0], n) * 10.0 ** rng.uniform(-30, 30, n)).astype(np.float32)
+    if kind == "subnormal":
+        return (rng.integers(-1000, 1000, n) * np.float32(1e-42)).astype(np.float32)
+    if kind == "nan":
+        x = rng.standard_normal(n).astype(np.float32)
+        bits = x.view(np.uint32)
+        pos = rng.random(n) < 0.02
+        neg = rng.random(n) < 0.02
+        bits[pos] = 0x7FC00000 | rng.integers(0, 1 << 22, int(pos.sum())).astype(np.uint32)
+        bits[neg] = 0xFFC00000 | rng.integers(0, 1 << 22, int(neg.sum())).astype(np.uint32)
+        x[rng.random(n) < 0.01] = np.inf
+        return x
+    raise ValueError(kind)
+
+
+def bit_order_topk(vals, k):
+    """The k positions first in the header's order for NaN-holding rows: the fp32 bit
+    pattern mapped onto an unsigned order (-0.0 folded onto +0.0), ties by position."""
+    u = vals.view(np.uint32).astype(np.int64)
+    u = np.where(u == 0x80000000, 0, u)
+    key = np.where(u >= 0x80000000, 0xFFFFFFFF - u, u + 0x80000000)
+    order = np.lexsort((np.arange(u.size), -key))
+    return np.sort(order[:min(k, u.size)])
+
+
+def run_case(L, k, specs, seed):
+    """specs: list of (kind, nv). One call to mqa_topk over all rows."""
+    rng = np.random.default_rng(seed)
+    rows = len(specs)
+    logits = np.full((rows, L), np.nan, np.float32)  # beyond nv: never read as a value
+    for r, (kind, nv) in enumerate(specs):
+        logits[r, :nv] = crafted_row(kind, nv, rng)
+    ctx = np.array([nv for _, nv in specs], np.int32)
+    shape = mqa.make_shape(rows, 1, 64, L, L)
+    d_logits = torch.from_numpy(logits).cuda()
+    d_ctx = torch.from_numpy(ctx).cuda()
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+    nbytes = mqa.mqa_topk_workspace_bytes(shape, L, k)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    mqa.mqa_topk(d_logits, d_ctx, L, k, idx, shape, ws)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for r, (kind, nv) in enumerate(specs):
+        vals = logits[r, :nv]
+        want = bit_order_topk(vals, k) if kind == "nan" else oracle.topk_row(vals.astype(np.float64), k)
+        m = min(k, nv)
+        assert np.all(got[r, m:] == -1), f"{kind} nv={nv} k={k}: padding"
+        sel = np.sort(got[r, :m])
+        assert np.array_equal(sel, want), (
+            f"{kind} nv={nv} k={k}: {np.setdiff1d(sel, want).size} positions differ from the expected set")
+
+
+@pytest.mark.parametrize("k", [2048, 1, 100, 2047])
+def test_topk_rows_fit_one_workgroup(k):
+    nvs = sorted({1, 2048, 2049, 3000, 4097, 8192} | {k + 1})
+    specs = [(kind, nv) for kind in KINDS for nv in nvs if nv <= 8192]
+    say(f"[gpu] topk crafted rows L=8192 k={k} rows={len(specs)}")
+    run_case(8192, k, specs, seed=7000 + k)
+
+
+@pytest.mark.parametrize("k", [2048, 300])
+def test_topk_long_rows(k):
+    nvs = [5, 2049, 8192, 8193, 20000, 40000]
+    specs = [(kind, nv) for kind in KINDS for nv in nvs]
+    say(f"[gpu] topk crafted rows L=40000 k={k} rows={len(specs)}")
+    run_case(40000, k, specs, seed=7100 + k)
