@@ -94,7 +94,7 @@ __device__ __forceinline__ int visible(const Params& p, int row) {
 // Per-wave scratch slots, one region per use so that consecutive block operations need
 // no barrier between them for the scratch itself.
 enum { kRedLo = 0, kRedHi = kWaves, kRedBad = 2 * kWaves, kRedBin = 3 * kWaves, kRedEmit = 4 * kWaves,
-       kRedSize = 5 * kWaves };
+       kRedCand = 5 * kWaves, kRedSize = 6 * kWaves };
 
 struct Core {
   uint32_t hist[kKeyBins];
@@ -104,13 +104,6 @@ struct Core {
 
 struct Full : Core {
   uint64_t cand[kCap];
-};
-
-// A short row's selected positions are gathered here (LDS slots in any order) and
-// written to the output row in one coalesced pass at the end: scattered 4-byte global
-// stores from every lane cost more than the LDS round trip.
-struct Rows : Full {
-  int32_t sel[kChunk + 64];  // + one dummy slot per lane
 };
 
 // Wave-aggregated append to an LDS counter. Must be called by all 64 lanes of a wave.
@@ -232,17 +225,16 @@ __device__ __forceinline__ void load_chunk(const float* row, int base, int nv, f
 }
 
 // Selects the `rem` largest of the n candidates in sh.cand by counting, for each, the
-// candidates above it. n <= kRankMax.
+// candidates above it; e is unique, so a selected candidate's rank is its slot after the
+// sh.n_out positions already emitted. n <= kRankMax.
 __device__ void rank_select(Full& sh, int n, uint32_t rem, int32_t* out, int k) {
+  const uint32_t base = sh.n_out;
   for (int i = threadIdx.x; i < n; i += kThreads) {
     const uint64_t e = sh.cand[i];
     uint32_t rank = 0;
 #pragma unroll 8
     for (int j = 0; j < n; ++j) rank += sh.cand[j] > e ? 1u : 0u;
-    if (rank < rem) {
-      const uint32_t slot = atomicAdd(&sh.n_out, 1u);
-      if (slot < (uint32_t)k) out[slot] = position(e);
-    }
+    if (rank < rem && base + rank < (uint32_t)k) out[base + rank] = position(e);
   }
   __syncthreads();
 }
@@ -310,9 +302,9 @@ __device__ void select_trivial_row(const Params& p, int r, int nv) {
   for (int i = threadIdx.x; i < p.k; i += kThreads) out[i] = i < nv ? i : -1;
 }
 
-// Sum over lanes 0..15 of a wave of v (min or max for the float forms): row-0 DPP
-// shifts, lane 15 ends with the result, which is returned to every lane.
-__device__ __forceinline__ uint32_t row16_sum(uint32_t v) {
+// Inclusive prefix sum within each 16-lane row of a wave (row-0 DPP shifts): lane l of
+// row 0 ends with the sum of lanes 0..l.
+__device__ __forceinline__ uint32_t row16_prefix(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
@@ -320,6 +312,7 @@ __device__ __forceinline__ uint32_t row16_sum(uint32_t v) {
   return v;
 }
 
+// Minimum (maximum) over lanes 0..15, returned to every lane.
 template <bool Max>
 __device__ __forceinline__ float row16_minmax(float v) {
   v = minmax_step<Max, 0x111, 0xf>(v);
@@ -357,11 +350,7 @@ __device__ __forceinline__ void threshold_bin(Core& sh, uint32_t rem, uint32_t& 
   // Wave totals in lanes 0..15; the owner is the first wave whose inclusive prefix
   // reaches rem.
   const uint32_t wt = lane < kWaves ? sh.red[kRedBin + lane] : 0u;
-  uint32_t wi = wt;
-  wi += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wi, 0x111, 0xf, 0xf, false);
-  wi += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wi, 0x112, 0xf, 0xf, false);
-  wi += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wi, 0x114, 0xf, 0xf, false);
-  wi += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wi, 0x118, 0xf, 0xf, false);
+  const uint32_t wi = row16_prefix(wt);
   const uint64_t reach = __ballot(lane < kWaves && wi >= rem);
   const int ow = __builtin_ctzll(reach);  // rem <= total: some wave reaches it
   const uint32_t ow_before = (uint32_t)__builtin_amdgcn_readlane((int)(wi - wt), ow);
@@ -397,7 +386,7 @@ __device__ __forceinline__ void threshold_bin(Core& sh, uint32_t rem, uint32_t& 
 // of the row sits in thread t's register i. Loads past nv are clamped onto the last
 // visible element, which leaves min, max and finiteness unchanged; histogram and emit
 // count only the elements below nv.
-__device__ void select_short_row(const Params& p, int r, int nv, Rows& sh) {
+__device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
   const int k = p.k;
   const float* row = p.logits + (int64_t)r * p.L;
   int32_t* out = p.idx + (int64_t)r * k;
@@ -414,10 +403,6 @@ __device__ void select_short_row(const Params& p, int r, int nv, Rows& sh) {
     v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
   }
   for (int i = threadIdx.x; i < kKeyBins; i += kThreads) sh.hist[i] = 0;
-  if (threadIdx.x == 0) {  // emit counters; the first use is several barriers later
-    sh.n_out = 0;
-    sh.n_cand = 0;
-  }
   // Min / max of the visible values; a non-finite value anywhere switches to key bins
   // (the wave reports it as an infinite maximum).
   float lo = __builtin_inff(), hi = -__builtin_inff();
@@ -473,10 +458,11 @@ __device__ void select_short_row(const Params& p, int r, int nv, Rows& sh) {
   const uint32_t rem = (uint32_t)k - above;
   const bool whole = cnt0 == rem;
   // Emit the elements above the threshold bin (the whole bin too when it is all taken)
-  // and collect the bin's own elements into the candidate list. Slots come from one LDS
-  // atomic per wave and counter plus the lane's rank in the wave's mask; lanes that emit
-  // nothing write a private dummy slot. above(bin0) < k and the bin holds at most
-  // nv <= kCap elements, so every slot is in range.
+  // straight to the output row and collect the bin's own elements into the candidate
+  // list. Each wave counts its elements and publishes the counts; after one barrier every
+  // wave takes its first slots from a prefix over the 16 counts and each lane its rank
+  // in the wave's mask. above(bin0) < k and the bin holds at most nv <= kCap elements,
+  // so every slot is in range.
   const uint32_t thr = whole ? bin0 : bin0 + 1;
   uint64_t ma[kPer];
   uint32_t na = 0, nb = 0;
@@ -486,18 +472,21 @@ __device__ void select_short_row(const Params& p, int r, int nv, Rows& sh) {
     na += (uint32_t)__popcll(ma[i]);
     nb += whole ? 0u : (uint32_t)__popcll(__ballot(bin[i] == bin0) & inm[i]);
   }
-  uint32_t oa = 0, ob = 0;
   if (lane == 0) {
-    oa = atomicAdd(&sh.n_out, na);
-    if (nb) ob = atomicAdd(&sh.n_cand, nb);
+    sh.red[kRedEmit + wave] = na;
+    sh.red[kRedCand + wave] = nb;
   }
-  oa = __builtin_amdgcn_readfirstlane(oa);
-  ob = __builtin_amdgcn_readfirstlane(ob);
+  if (threadIdx.x == 0) sh.n_out = above;  // the finish appends after the emitted elements
+  __syncthreads();
+  const uint32_t ca = lane < kWaves ? sh.red[kRedEmit + lane] : 0u;
+  const uint32_t cb = lane < kWaves ? sh.red[kRedCand + lane] : 0u;
+  uint32_t oa = (uint32_t)__builtin_amdgcn_readlane((int)(row16_prefix(ca) - ca), wave);
+  uint32_t ob = (uint32_t)__builtin_amdgcn_readlane((int)(row16_prefix(cb) - cb), wave);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int t = i * kThreads + tid;
     const uint32_t ra = __builtin_amdgcn_mbcnt_hi((uint32_t)(ma[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma[i], oa));
-    sh.sel[__builtin_amdgcn_inverse_ballot_w64(ma[i]) ? ra : (uint32_t)(kChunk + lane)] = t;
+    if (__builtin_amdgcn_inverse_ballot_w64(ma[i])) out[ra] = t;
     oa += (uint32_t)__popcll(ma[i]);
     if (nb) {  // the threshold bin's elements (few)
       const uint64_t mb = __ballot(bin[i] == bin0) & inm[i];
@@ -508,22 +497,20 @@ __device__ void select_short_row(const Params& p, int r, int nv, Rows& sh) {
       }
     }
   }
-  __syncthreads();
   if (!whole) {
+    __syncthreads();  // the candidate list is complete
     // Key bins fix the top 12 bits of e; linear or single bins fix none.
     const uint64_t prefix = keyed ? (uint64_t)bin0 << (64 - kKeyBits) : 0ull;
     const uint64_t pmask = keyed ? (uint64_t)(kKeyBins - 1) << (64 - kKeyBits) : 0ull;
-    finish_candidates(sh, (int)cnt0, prefix, pmask, keyed ? 64 - kKeyBits : 64, rem, sh.sel, k);
+    finish_candidates(sh, (int)cnt0, prefix, pmask, keyed ? 64 - kKeyBits : 64, rem, out, k);
   }
-  // k < nv: exactly k slots were filled, and both branches above end at a barrier.
-  for (int i = threadIdx.x; i < k; i += kThreads) out[i] = sh.sel[i];
 }
 
 // Pass 1. Implicit mode (no workspace): workgroup r handles row r. Scheduled mode:
 // persistent workgroups walk long-row chunks (histograms), then short rows, then
 // trivial rows.
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
-  __shared__ Rows sh;
+  __shared__ Full sh;
   if (p.meta == nullptr) {
     const int r = blockIdx.x;
     const int nv = visible(p, r);
