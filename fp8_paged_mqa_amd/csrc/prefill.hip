@@ -26,8 +26,11 @@
 //     the fp8 sign bits, exact) into the other buffer and loads its bytes of stage s+2,
 //     then the waves compute stage s: the conversion and LDS writes overlap the MFMAs.
 //     One barrier per stage.
-//   * LDS layout per 32-key tile: [k-step 0..7][lane 0..63][8 f16], so each k-step's B
-//     operands are one conflict-free 1 KB ds_read_b128 per wave.
+//   * LDS layout per 32-key tile: [k-step 0..7][slot 0..63][8 f16], lane L's operand of
+//     k-step st in slot L ^ (2*(st/2) + 8*(L/32)). Each k-step's B operands are one
+//     1 KB ds_read_b128 per wave (the XOR permutes lanes within aligned 16-lane groups,
+//     so the read stays conflict-free), and the eight threads that convert one key's
+//     16-byte pieces write eight different bank slots (unswizzled, they all hit one).
 //   * Epilogue: a lane's 16 results are heads 8q + 4h + r (q, r < 4) of key j; relu,
 //     weights and the head sum run in registers, one permlane32 swap adds the two lane
 //     halves, then |scale| and the window mask. Each 32-key group's epilogue runs one
@@ -203,7 +206,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_logits_kernel(Params p) {
   static_assert(kPieces * kThreads * 16 == kStage * kD, "a stage is whole 16-byte pieces");
   const int lk = threadIdx.x >> 3;
   const int lb = (threadIdx.x & 7) * 16;
-  const int dst_off = ((threadIdx.x & 3) * 2) * 1024 + ((lb >> 6) * 32 + (lk & 31)) * 16;
+  const int dst_off = ((threadIdx.x & 3) * 2) * 1024 +
+                      ((((lb >> 6) * 32 + (lk & 31)) ^ (2 * (threadIdx.x & 3) + 8 * (lb >> 6))) * 16);
   auto fetch = [&](int s0, i32x4 (&raw)[kPieces], float (&sc)[kPieces]) {
 #pragma unroll
     for (int e = 0; e < kPieces; ++e) {
@@ -283,12 +287,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_logits_kernel(Params p) {
     if (s0 + kStage < c1) stash(buf ^ 1, raw, sc);
     if (s0 + 2 * kStage < c1) fetch(s0 + 2 * kStage, raw, sc);
     const uint8_t* const bop = bops[buf];
+    // Slot of this lane's operand in k-step rows 2c and 2c+1.
+    int slot[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) slot[c] = (lane ^ (2 * c + 8 * h)) * 16;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {  // two 32-key tiles per stage
       Operand8 kb;
 #pragma unroll
       for (int st = 0; st < 8; ++st)
-        kb.k[st] = *reinterpret_cast<const f16x8*>(bop + u * kTileBytes + st * 1024 + lane * 16);
+        kb.k[st] = *reinterpret_cast<const f16x8*>(bop + u * kTileBytes + st * 1024 + slot[st >> 1]);
       f32x16 accC[TILES];
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
