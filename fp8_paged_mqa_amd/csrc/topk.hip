@@ -35,7 +35,9 @@
 //            reserves the output slots) and collect its threshold-bin elements, and
 //            finish each row's candidates in LDS. If the threshold bin holds more than
 //            kCap elements (extreme ties, e.g. a constant row) the finish refines over
-//            the whole row from global memory: slower, same result.
+//            the whole row from global memory: slower, same result. The short and
+//            trivial rows of such a call are selected by the finishing pass's spare
+//            workgroups.
 // When max_model_len <= 8192 no row can be long: one launch, one workgroup per row.
 #include <hip/hip_runtime.h>
 
@@ -507,8 +509,9 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
 }
 
 // Pass 1. Implicit mode (no workspace): workgroup r handles row r. Scheduled mode:
-// persistent workgroups walk long-row chunks (histograms), then short rows, then
-// trivial rows.
+// persistent workgroups walk the long rows' chunks (histograms); the short and trivial
+// rows wait for the last pass, whose workgroups are mostly idle otherwise, so that they
+// do not lengthen this one.
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
   __shared__ Full sh;
   if (p.meta == nullptr) {
@@ -519,10 +522,8 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
     return;
   }
   const int nc = (int)p.meta[kMetaChunks];
-  const int ns = (int)p.meta[kMetaShort];
-  const int nt = (int)p.meta[kMetaTrivial];
-  for (int item = blockIdx.x; item < nc + ns + nt; item += gridDim.x) {
-    if (item < nc) {
+  for (int item = blockIdx.x; item < nc; item += gridDim.x) {
+    {
       const int slot = (int)p.chunk_items[2 * item];
       const int ch = (int)p.chunk_items[2 * item + 1];
       const int r = (int)p.long_rows[slot];
@@ -541,13 +542,6 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         if (c) atomicAdd(&gh[i], c);
       }
       __syncthreads();
-    } else if (item < nc + ns) {
-      const int r = (int)p.short_rows[item - nc];
-      select_short_row(p, r, visible(p, r), sh);
-      __syncthreads();
-    } else {
-      const int r = (int)p.triv_rows[item - nc - ns];
-      select_trivial_row(p, r, visible(p, r));
     }
   }
 }
@@ -674,11 +668,26 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(Params p) {
   }
 }
 
-// Pass 3 (long rows): refine each row's candidates.
+// Pass 3: refine each long row's candidates; then the short rows (whole selection) and
+// the trivial rows.
 __global__ __launch_bounds__(kThreads) void topk_finish_kernel(Params p) {
   __shared__ Full sh;
   const int nl = (int)p.meta[kMetaLong];
-  for (int slot = blockIdx.x; slot < nl; slot += gridDim.x) {
+  const int ns = (int)p.meta[kMetaShort];
+  const int nt = (int)p.meta[kMetaTrivial];
+  for (int item = blockIdx.x; item < nl + ns + nt; item += gridDim.x) {
+    if (item >= nl) {  // uniform
+      if (item < nl + ns) {
+        const int r = (int)p.short_rows[item - nl];
+        select_short_row(p, r, visible(p, r), sh);
+        __syncthreads();
+      } else {
+        const int r = (int)p.triv_rows[item - nl - ns];
+        select_trivial_row(p, r, visible(p, r));
+      }
+      continue;
+    }
+    const int slot = item;
     const int r = (int)p.long_rows[slot];
     const int nv = visible(p, r);
     const int k = p.k;
