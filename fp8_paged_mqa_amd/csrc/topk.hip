@@ -508,6 +508,32 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
   }
 }
 
+// One 8192-element chunk of a long row: element i*kThreads + threadIdx.x of
+// [base, base + kChunk) in register i (loads past the row's visible end are clamped onto
+// its last visible element), and where the chunk belongs.
+struct Chunk {
+  int slot, r, nv, base;
+  float v[kPer];
+};
+
+// Issues the loads of chunk item `item`; nothing waits for them here, so the caller can
+// prefetch the next item while it works on the current one.
+__device__ __forceinline__ void fetch_chunk(const Params& p, int item, Chunk& c) {
+  c.slot = (int)p.chunk_items[2 * item];
+  c.base = (int)p.chunk_items[2 * item + 1] * kChunk;
+  c.r = (int)p.long_rows[c.slot];
+  c.nv = visible(p, c.r);
+  const int n = min(kChunk, c.nv - c.base);  // >= 1: chunks start below nv
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p.logits + (int64_t)c.r * p.L + c.base), 0, n * 4, 0x00020000);
+  const uint32_t last = (uint32_t)(n - 1) * 4u;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const uint32_t off = min((uint32_t)threadIdx.x * 4u + (uint32_t)(i * kThreads * 4), last);
+    c.v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+  }
+}
+
 // Pass 1. Implicit mode (no workspace): workgroup r handles row r. Scheduled mode:
 // persistent workgroups walk the long rows' chunks (histograms); the short and trivial
 // rows wait for the last pass, whose workgroups are mostly idle otherwise, so that they
@@ -522,27 +548,27 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
     return;
   }
   const int nc = (int)p.meta[kMetaChunks];
+  if ((int)blockIdx.x >= nc) return;
+  const int tid = (int)threadIdx.x;
+  Chunk cur, nxt;
+  fetch_chunk(p, blockIdx.x, cur);
+  clear_hist(sh, kKeyBins);
   for (int item = blockIdx.x; item < nc; item += gridDim.x) {
-    {
-      const int slot = (int)p.chunk_items[2 * item];
-      const int ch = (int)p.chunk_items[2 * item + 1];
-      const int r = (int)p.long_rows[slot];
-      const int nv = visible(p, r);
-      const int base = ch * kChunk;
-      float v[kPer];
-      load_chunk(p.logits + (int64_t)r * p.L, base, nv, v);
-      clear_hist(sh, kKeyBins);
+    if (item + (int)gridDim.x < nc) fetch_chunk(p, item + gridDim.x, nxt);  // uniform
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (base + i * kThreads + (int)threadIdx.x < nv) atomicAdd(&sh.hist[order_key(v[i]) >> (32 - kKeyBits)], 1u);
-      __syncthreads();
-      uint32_t* gh = p.hist + (int64_t)slot * kKeyBins;
-      for (int i = threadIdx.x; i < kKeyBins; i += kThreads) {
-        const uint32_t c = sh.hist[i];
-        if (c) atomicAdd(&gh[i], c);
-      }
-      __syncthreads();
+    for (int i = 0; i < kPer; ++i)
+      if (__builtin_amdgcn_inverse_ballot_w64(__ballot(tid < cur.nv - cur.base - i * kThreads)))
+        atomicAdd(&sh.hist[order_key(cur.v[i]) >> (32 - kKeyBits)], 1u);
+    __syncthreads();
+    // Add the chunk's bins into the row's histogram, clearing them for the next chunk.
+    uint32_t* gh = p.hist + (int64_t)cur.slot * kKeyBins;
+    for (int i = tid; i < kKeyBins; i += kThreads) {
+      const uint32_t c = sh.hist[i];
+      sh.hist[i] = 0;
+      if (c) atomicAdd(&gh[i], c);
     }
+    __syncthreads();
+    cur = nxt;
   }
 }
 
@@ -622,49 +648,80 @@ __global__ __launch_bounds__(kThreads) void topk_schedule_kernel(Params p) {
 __global__ __launch_bounds__(kThreads) void topk_split_kernel(Params p) {
   __shared__ Core sh;
   const int nc = (int)p.meta[kMetaChunks];
+  if ((int)blockIdx.x >= nc) return;
+  const int k = p.k;
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The row histogram arrives 16 bytes per thread (kKeyBins = 4 * kThreads).
+  static_assert(kKeyBins == 4 * kThreads, "one uint4 of the histogram per thread");
+  auto fetch_hist = [&](int slot) {
+    return reinterpret_cast<const uint4*>(p.hist + (int64_t)slot * kKeyBins)[tid];
+  };
+  Chunk cur, nxt;
+  fetch_chunk(p, blockIdx.x, cur);
+  uint4 hcur = fetch_hist(cur.slot), hnxt;
   for (int item = blockIdx.x; item < nc; item += gridDim.x) {
-    const int slot = (int)p.chunk_items[2 * item];
-    const int ch = (int)p.chunk_items[2 * item + 1];
-    const int r = (int)p.long_rows[slot];
-    const int nv = visible(p, r);
-    const int k = p.k;
-    const int base = ch * kChunk;
-    float v[kPer];
-    load_chunk(p.logits + (int64_t)r * p.L, base, nv, v);
-    const uint32_t* gh = p.hist + (int64_t)slot * kKeyBins;
-    for (int i = threadIdx.x; i < kKeyBins; i += kThreads) sh.hist[i] = gh[i];
+    if (item + (int)gridDim.x < nc) {  // uniform: prefetch the next item
+      fetch_chunk(p, item + gridDim.x, nxt);
+      hnxt = fetch_hist(nxt.slot);
+    }
+    reinterpret_cast<uint4*>(sh.hist)[tid] = hcur;
     __syncthreads();
-    find_bin(sh, kKeyBins, (uint32_t)k);
-    const uint32_t bin0 = sh.bin;
-    const bool whole = sh.hist[bin0] == (uint32_t)k - sh.above;
-    uint32_t key[kPer];
+    uint32_t bin0, above, cnt0;
+    threshold_bin<kKeyBins / kThreads>(sh, (uint32_t)k, bin0, above, cnt0);
+    const bool whole = cnt0 == (uint32_t)k - above;
+    // Elements above the threshold bin (the whole bin too when all of it is taken) go to
+    // the output, the bin's own elements to the row's candidate list; slots from one
+    // pair of global atomics per workgroup, a prefix over the waves' counts and the
+    // lanes' ranks in the ballot masks.
+    const uint32_t thr = whole ? bin0 : bin0 + 1;
+    uint64_t ma[kPer], mb[kPer];
     uint32_t na = 0, nb = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      key[i] = order_key(v[i]);
-      const uint32_t d = key[i] >> (32 - kKeyBits);
-      const bool in = base + i * kThreads + (int)threadIdx.x < nv;
-      na += (in && (d > bin0 || (whole && d == bin0))) ? 1u : 0u;
-      nb += (in && !whole && d == bin0) ? 1u : 0u;
+      const uint64_t in = __ballot(tid < cur.nv - cur.base - i * kThreads);
+      const uint32_t d = order_key(cur.v[i]) >> (32 - kKeyBits);
+      ma[i] = __ballot(d >= thr) & in;
+      mb[i] = whole ? 0ull : (__ballot(d == bin0) & in);
+      na += (uint32_t)__popcll(ma[i]);
+      nb += (uint32_t)__popcll(mb[i]);
     }
-    uint32_t oa, ob;
-    block_reserve2(na, nb, &p.counters[2 * slot], &p.counters[2 * slot + 1], sh, oa, ob);
-    int32_t* out = p.idx + (int64_t)r * k;
-    uint64_t* cand = p.cand + (int64_t)slot * kCap;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int t = base + i * kThreads + (int)threadIdx.x;
-      const uint32_t d = key[i] >> (32 - kKeyBits);
-      const bool in = t < nv;
-      if (in && (d > bin0 || (whole && d == bin0))) {
-        if (oa < (uint32_t)k) out[oa] = t;
-        ++oa;
-      } else if (in && !whole && d == bin0) {
-        if (ob < (uint32_t)kCap) cand[ob] = compose(key[i], t);
-        ++ob;
-      }
+    if (lane == 0) {
+      sh.red[kRedEmit + wave] = na;
+      sh.red[kRedCand + wave] = nb;
     }
     __syncthreads();
+    const uint32_t ca = lane < kWaves ? sh.red[kRedEmit + lane] : 0u;
+    const uint32_t cb = lane < kWaves ? sh.red[kRedCand + lane] : 0u;
+    const uint32_t ia = row16_prefix(ca), ib = row16_prefix(cb);
+    if (tid == 0) {
+      const uint32_t ta = (uint32_t)__builtin_amdgcn_readlane((int)ia, kWaves - 1);
+      const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)ib, kWaves - 1);
+      sh.base_a = ta ? atomicAdd(&p.counters[2 * cur.slot], ta) : 0u;
+      sh.base_b = tb ? atomicAdd(&p.counters[2 * cur.slot + 1], tb) : 0u;
+    }
+    __syncthreads();
+    uint32_t oa = sh.base_a + (uint32_t)__builtin_amdgcn_readlane((int)(ia - ca), wave);
+    uint32_t ob = sh.base_b + (uint32_t)__builtin_amdgcn_readlane((int)(ib - cb), wave);
+    int32_t* out = p.idx + (int64_t)cur.r * k;
+    uint64_t* cand = p.cand + (int64_t)cur.slot * kCap;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int t = cur.base + i * kThreads + tid;
+      const uint32_t ra = __builtin_amdgcn_mbcnt_hi((uint32_t)(ma[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma[i], oa));
+      if (__builtin_amdgcn_inverse_ballot_w64(ma[i]) && ra < (uint32_t)k) out[ra] = t;
+      oa += (uint32_t)__popcll(ma[i]);
+      if (mb[i]) {  // uniform; the threshold bin's elements (few)
+        const uint32_t rb = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb[i], ob));
+        if (__builtin_amdgcn_inverse_ballot_w64(mb[i]) && rb < (uint32_t)kCap) cand[rb] = compose(order_key(cur.v[i]), t);
+        ob += (uint32_t)__popcll(mb[i]);
+      }
+    }
+    // The next item's first LDS writes (histogram, then the slots above) come after
+    // barriers every wave passes only once it has read this item's.
+    cur = nxt;
+    hcur = hnxt;
   }
 }
 
@@ -692,14 +749,12 @@ __global__ __launch_bounds__(kThreads) void topk_finish_kernel(Params p) {
     const int nv = visible(p, r);
     const int k = p.k;
     const uint32_t* gh = p.hist + (int64_t)slot * kKeyBins;
-    for (int i = threadIdx.x; i < kKeyBins; i += kThreads) sh.hist[i] = gh[i];
+    reinterpret_cast<uint4*>(sh.hist)[threadIdx.x] = reinterpret_cast<const uint4*>(gh)[threadIdx.x];
     __syncthreads();
-    find_bin(sh, kKeyBins, (uint32_t)k);
-    const uint32_t bin0 = sh.bin;
-    const uint32_t above = sh.above;
+    uint32_t bin0, above, cnt0;
+    threshold_bin<kKeyBins / kThreads>(sh, (uint32_t)k, bin0, above, cnt0);
     const uint32_t rem = (uint32_t)k - above;
-    const uint32_t cnt0 = sh.hist[bin0];
-    __syncthreads();
+    __syncthreads();  // every wave is done with the histogram before the next item's copy
     if (cnt0 == rem) continue;  // the split pass took the whole bin (uniform)
     const float* row = p.logits + (int64_t)r * p.L;
     int32_t* out = p.idx + (int64_t)r * k;
