@@ -98,17 +98,32 @@ __global__ __launch_bounds__(kThreads) void k_write_kernel(const void* __restric
     const float amax = row_max(m);
     const float scale = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
     uint32_t lo = 0, hi = 0;
+    if (__builtin_isfinite(amax) && scale > 0.0f) {
+      // Every quotient is finite (|x / scale| <= 448 up to rounding): gfx950's packed
+      // conversion rounds to the nearest code, ties to even, and overflows past the 464
+      // tie to NaN keeping the sign, which is the rule above (checked against the
+      // encoder on every code, every midpoint and their float neighbours, subnormal
+      // quotients included). Only a NaN quotient would differ (it returns 0xFF), and
+      // none occurs here.
+      float y[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo |= encode_e4m3fn(__fdiv_rn(x[j], scale)) << (8 * j);
-      hi |= encode_e4m3fn(__fdiv_rn(x[4 + j], scale)) << (8 * j);
+      for (int j = 0; j < 8; ++j) y[j] = __fdiv_rn(x[j], scale);
+      lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false), true);
+      hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false), true);
+    } else {  // a non-finite key, or a scale that underflows to zero
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo |= encode_e4m3fn(__fdiv_rn(x[j], scale)) << (8 * j);
+        hi |= encode_e4m3fn(__fdiv_rn(x[4 + j], scale)) << (8 * j);
+      }
     }
     if (base + r < T && slot >= 0 && slot < nslots) {
       uint8_t* row = kv + slot * kRow;
       // rows are 4-byte aligned: two dword stores
       reinterpret_cast<uint32_t*>(row)[2 * c] = lo;
       reinterpret_cast<uint32_t*>(row)[2 * c + 1] = hi;
-      if (c == 0) *reinterpret_cast<float*>(row + kD) = scale;
+      // A NaN scale (a NaN key) is written as the canonical quiet NaN.
+      if (c == 0) *reinterpret_cast<float*>(row + kD) = __builtin_isnan(scale) ? __builtin_nanf("") : scale;
     }
   }
 }

@@ -177,7 +177,8 @@ enum { MQA_DTYPE_BF16 = 0, MQA_DTYPE_F32 = 1 };
  *     scale = amax / 448 in fp32, correctly rounded (scale = 1 when amax = 0)
  *     code  = e4m3fn(k[t, i] / scale): the fp32 quotient, correctly rounded, then the
  *             nearest e4m3fn value, ties to even (so |code| <= 448; a NaN key makes
- *             the row NaN, an infinite key gives an infinite scale)
+ *             the row NaN, with the scale written as the quiet NaN 0x7FC00000; an
+ *             infinite key gives an infinite scale; -0.0 keeps its sign, code 0x80)
  * and writes row slot_mapping[t] (row blk * block_size + offset of a blocked cache):
  *     kv_cache[slot*132 + 0 .. 127] = codes, kv_cache[slot*132 + 128 .. 131] = scale.
  * Tokens whose slot lies outside [0, num_slots) are skipped (negative slots mark

@@ -220,7 +220,8 @@ def topk(logits, context_lens, next_n, k, max_model_len=None):
 # that scale; the reading taken here is the per-token absolute maximum mapped
 # onto the largest finite e4m3fn value: scale = amax / 448 in fp32, codes =
 # e4m3fn(x / scale) with x / scale computed in fp32 and rounded to nearest even.
-# A row of zeros gets scale 1 and zero codes. NaN inputs give NaN codes and
+# A row of zeros gets scale 1 and the codes of its zeros (-0.0 is code 0x80, as
+# everywhere else). NaN inputs give NaN codes and
 # scale; an input of infinite magnitude gives an infinite scale.
 # ---------------------------------------------------------------------------
 E4M3FN_MAX = 448.0
@@ -255,8 +256,8 @@ def quantize_k_row(k_row) -> tuple[np.ndarray, np.float32]:
     """One token's 128 keys (float32 values) -> (128 e4m3fn codes, fp32 scale)."""
     k32 = np.asarray(k_row, dtype=np.float32)
     amax = np.float32(np.max(np.abs(k32))) if not np.isnan(k32).any() else np.float32(np.nan)
-    if amax == 0:
-        return np.zeros(k32.shape, dtype=np.uint8), np.float32(1.0)
+    if amax == 0:  # scale 1: the codes of the zeros themselves (-0.0 keeps its sign)
+        return encode_e4m3fn(k32.astype(np.float64)), np.float32(1.0)
     scale = np.float32(amax / np.float32(E4M3FN_MAX))       # fp32 division
     scaled = (k32 / scale).astype(np.float32)                # fp32 division per element
     return encode_e4m3fn(scaled.astype(np.float64)), scale

@@ -375,6 +375,11 @@ def pin_quantize_round_trip(orc):
         assert TORCH_E4M3[codes[i]] == (448.0 if k[i] > 0 else -448.0)
     codes, scale = orc.quantize_k_row(np.zeros(128, np.float32))
     assert np.all(codes == 0) and scale == np.float32(1.0)
+    # signed zeros keep their sign through scale 1, as torch's own cast does
+    z = np.where(np.arange(128) % 3 == 0, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+    codes, scale = orc.quantize_k_row(z)
+    want = torch.from_numpy(z).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert scale == np.float32(1.0) and np.array_equal(codes, want) and want[0] == 0x80
 
 
 def pin_write_slots_and_logits(orc):

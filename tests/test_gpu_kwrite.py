@@ -17,7 +17,13 @@ def _keys(rng, T, dtype):
     mag = rng.lognormal(0.0, 2.0, size=(T, 1)).astype(np.float32)
     k = (rng.standard_normal((T, 128)).astype(np.float32) * mag)
     special = [np.zeros(128), np.r_[np.zeros(127), [3.0]], np.full(128, -2.5), np.linspace(-1e-30, 1e-30, 128),
-               np.linspace(-1e30, 1e30, 128), (np.arange(128) % 9 - 4) * 2.0 ** -12]
+               np.linspace(-1e30, 1e30, 128), (np.arange(128) % 9 - 4) * 2.0 ** -12,
+               # rows the hardware conversion must not take: a NaN key, infinite keys, and
+               # a largest magnitude so small that amax / 448 underflows to zero
+               np.r_[[np.nan], np.linspace(-3, 3, 127)], np.r_[[np.inf], np.ones(127)],
+               np.r_[np.ones(127), [-np.inf]], np.r_[[1.4e-45, -1.4e-45], np.zeros(126)],
+               # a subnormal largest magnitude with a nonzero (subnormal) scale
+               np.linspace(-1e-40, 1e-40, 128)]
     for i, row in enumerate(special):
         k[i] = row
     t = torch.from_numpy(k)
