@@ -101,7 +101,7 @@ enum { kRedLo = 0, kRedHi = kWaves, kRedBad = 2 * kWaves, kRedBin = 3 * kWaves, 
 struct Core {
   uint32_t hist[kKeyBins];
   uint32_t red[kRedSize];
-  uint32_t n_out, n_cand, bin, above, base_a, base_b;
+  uint32_t n_out, bin, above, base_a, base_b;
 };
 
 struct Full : Core {
@@ -200,30 +200,6 @@ __device__ void find_bin(Core& sh, int nbins, uint32_t rem) {
 __device__ __forceinline__ void clear_hist(Core& sh, int nbins) {
   for (int i = threadIdx.x; i < nbins; i += kThreads) sh.hist[i] = 0;
   __syncthreads();
-}
-
-// Reserves na (nb) consecutive slots of *ca (*cb) for each thread with one atomic per
-// counter for the whole block; returns this thread's first slots.
-__device__ void block_reserve2(uint32_t na, uint32_t nb, uint32_t* ca, uint32_t* cb, Core& sh,
-                               uint32_t& oa, uint32_t& ob) {
-  const uint32_t packed = (na << 16) | nb;  // na, nb <= kPer: block totals < 2^16
-  uint32_t tot;
-  const uint32_t excl = block_exclusive_scan(packed, sh, kRedEmit, tot);
-  if (threadIdx.x == 0) {
-    sh.base_a = atomicAdd(ca, tot >> 16);
-    sh.base_b = atomicAdd(cb, tot & 0xFFFFu);
-  }
-  __syncthreads();
-  oa = sh.base_a + (excl >> 16);
-  ob = sh.base_b + (excl & 0xFFFFu);
-  __syncthreads();
-}
-
-// Loads element i*1024 + tid of the chunk at `base` for i < kPer (addresses clamped
-// into the row; all loads issued before any is used).
-__device__ __forceinline__ void load_chunk(const float* row, int base, int nv, float (&v)[kPer]) {
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) v[i] = row[min(base + i * kThreads + (int)threadIdx.x, nv - 1)];
 }
 
 // Selects the `rem` largest of the n candidates in sh.cand by counting, for each, the
