@@ -38,7 +38,9 @@
 //            the whole row from global memory: slower, same result. The short and
 //            trivial rows of such a call are selected by the finishing pass's spare
 //            workgroups.
-// When max_model_len <= 8192 no row can be long: one launch, one workgroup per row.
+// When max_model_len <= 8192 no row can be long: one launch, one workgroup per row. Up to
+// 32768 the same holds with 32 logits per thread (a threshold bin of more than kCap
+// elements then refines over the row itself); only longer rows take the chunked passes.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -50,6 +52,8 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPer = 8;                   // logits per thread per chunk
 constexpr int kChunk = kThreads * kPer;   // 8192
+constexpr int kWidePer = 32;              // logits per thread of a whole-row select
+constexpr int kWide = kThreads * kWidePer;  // 32768: rows one workgroup selects alone
 constexpr int kLinBins = 2048;            // first level of a short row (linear bins)
 constexpr int kKeyBits = 12;              // first level of a long row (top key bits)
 constexpr int kKeyBins = 1 << kKeyBits;   // 4096
@@ -360,11 +364,14 @@ __device__ __forceinline__ void threshold_bin(Core& sh, uint32_t rem, uint32_t& 
   }
 }
 
-// Rows with k < nv <= kChunk: the whole select by one workgroup. Element i*kThreads + t
-// of the row sits in thread t's register i. Loads past nv are clamped onto the last
-// visible element, which leaves min, max and finiteness unchanged; histogram and emit
-// count only the elements below nv.
-__device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
+// Rows with k < nv <= PER * kThreads: the whole select by one workgroup. Element
+// i*kThreads + t of the row sits in thread t's register i. Loads past nv are clamped onto
+// the last visible element, which leaves min, max and finiteness unchanged; histogram and
+// emit count only the elements below nv. PER = 8 serves rows up to 8192 (every tie set
+// fits the candidate list); PER = 32 rows up to 32768, whose threshold bin can exceed the
+// list, in which case the finish refines over the row itself.
+template <int PER>
+__device__ void select_row(const Params& p, int r, int nv, Full& sh) {
   const int k = p.k;
   const float* row = p.logits + (int64_t)r * p.L;
   int32_t* out = p.idx + (int64_t)r * k;
@@ -374,9 +381,9 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, nv * 4, 0x00020000);
   const uint32_t last = (uint32_t)(nv - 1) * 4u;
-  float v[kPer];
+  float v[PER];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const uint32_t off = min((uint32_t)threadIdx.x * 4u + (uint32_t)(i * kThreads * 4), last);
     v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
   }
@@ -386,7 +393,7 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
   float lo = __builtin_inff(), hi = -__builtin_inff();
   uint64_t bad = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     lo = fminf(lo, v[i]);
     hi = fmaxf(hi, v[i]);
     bad |= __ballot(!__builtin_isfinite(v[i]));
@@ -410,23 +417,23 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
   const bool linear = !nonfinite && hi > lo && __builtin_isfinite(spread) && __builtin_isfinite(scale) && scale > 0.0f;
   const bool keyed = !linear && (nonfinite || hi > lo);
   const int tid = (int)threadIdx.x;
-  uint64_t inm[kPer];  // lanes whose element i is below nv
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) inm[i] = __ballot(tid < nv - i * kThreads);
-  uint32_t bin[kPer];
+  // Lanes whose element i is below nv (one compare; recomputed where needed, which costs
+  // less than holding 2 * PER scalar registers).
+  auto inm = [&](int i) { return __ballot(tid < nv - i * kThreads); };
+  uint32_t bin[PER];
   if (linear) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) bin[i] = min((uint32_t)(kLinBins - 1), (uint32_t)((v[i] - lo) * scale));
+    for (int i = 0; i < PER; ++i) bin[i] = min((uint32_t)(kLinBins - 1), (uint32_t)((v[i] - lo) * scale));
   } else if (keyed) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) bin[i] = order_key(v[i]) >> (32 - kKeyBits);
+    for (int i = 0; i < PER; ++i) bin[i] = order_key(v[i]) >> (32 - kKeyBits);
   } else {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) bin[i] = 0u;
+    for (int i = 0; i < PER; ++i) bin[i] = 0u;
   }
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (__builtin_amdgcn_inverse_ballot_w64(inm[i])) atomicAdd(&sh.hist[bin[i]], 1u);
+  for (int i = 0; i < PER; ++i)
+    if (__builtin_amdgcn_inverse_ballot_w64(inm(i))) atomicAdd(&sh.hist[bin[i]], 1u);
   __syncthreads();
   uint32_t bin0, above, cnt0;
   if (keyed)
@@ -439,16 +446,15 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
   // straight to the output row and collect the bin's own elements into the candidate
   // list. Each wave counts its elements and publishes the counts; after one barrier every
   // wave takes its first slots from a prefix over the 16 counts and each lane its rank
-  // in the wave's mask. above(bin0) < k and the bin holds at most nv <= kCap elements,
-  // so every slot is in range.
+  // in the wave's mask. above(bin0) < k, so every output slot is in range; candidate
+  // slots past kCap are dropped (the finish then refines over the row).
   const uint32_t thr = whole ? bin0 : bin0 + 1;
-  uint64_t ma[kPer];
   uint32_t na = 0, nb = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    ma[i] = __ballot(bin[i] >= thr) & inm[i];
-    na += (uint32_t)__popcll(ma[i]);
-    nb += whole ? 0u : (uint32_t)__popcll(__ballot(bin[i] == bin0) & inm[i]);
+  for (int i = 0; i < PER; ++i) {
+    const uint64_t in = inm(i);
+    na += (uint32_t)__popcll(__ballot(bin[i] >= thr) & in);
+    nb += whole ? 0u : (uint32_t)__popcll(__ballot(bin[i] == bin0) & in);
   }
   if (lane == 0) {
     sh.red[kRedEmit + wave] = na;
@@ -461,16 +467,18 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
   uint32_t oa = (uint32_t)__builtin_amdgcn_readlane((int)(row16_prefix(ca) - ca), wave);
   uint32_t ob = (uint32_t)__builtin_amdgcn_readlane((int)(row16_prefix(cb) - cb), wave);
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int t = i * kThreads + tid;
-    const uint32_t ra = __builtin_amdgcn_mbcnt_hi((uint32_t)(ma[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma[i], oa));
-    if (__builtin_amdgcn_inverse_ballot_w64(ma[i])) out[ra] = t;
-    oa += (uint32_t)__popcll(ma[i]);
+    const uint64_t in = inm(i);
+    const uint64_t ma = __ballot(bin[i] >= thr) & in;
+    const uint32_t ra = __builtin_amdgcn_mbcnt_hi((uint32_t)(ma >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma, oa));
+    if (__builtin_amdgcn_inverse_ballot_w64(ma)) out[ra] = t;
+    oa += (uint32_t)__popcll(ma);
     if (nb) {  // the threshold bin's elements (few)
-      const uint64_t mb = __ballot(bin[i] == bin0) & inm[i];
+      const uint64_t mb = __ballot(bin[i] == bin0) & in;
       if (mb) {
         const uint32_t rb = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, ob));
-        if (__builtin_amdgcn_inverse_ballot_w64(mb)) sh.cand[rb] = compose(order_key(v[i]), t);
+        if (__builtin_amdgcn_inverse_ballot_w64(mb) && rb < (uint32_t)kCap) sh.cand[rb] = compose(order_key(v[i]), t);
         ob += (uint32_t)__popcll(mb);
       }
     }
@@ -480,8 +488,30 @@ __device__ void select_short_row(const Params& p, int r, int nv, Full& sh) {
     // Key bins fix the top 12 bits of e; linear or single bins fix none.
     const uint64_t prefix = keyed ? (uint64_t)bin0 << (64 - kKeyBits) : 0ull;
     const uint64_t pmask = keyed ? (uint64_t)(kKeyBins - 1) << (64 - kKeyBits) : 0ull;
-    finish_candidates(sh, (int)cnt0, prefix, pmask, keyed ? 64 - kKeyBits : 64, rem, out, k);
+    const int top = keyed ? 64 - kKeyBits : 64;
+    if (PER * kThreads <= kCap || cnt0 <= (uint32_t)kCap) {  // uniform
+      finish_candidates(sh, (int)cnt0, prefix, pmask, top, rem, out, k);
+    } else if (keyed) {
+      refine<true>(sh, row, nv, prefix, pmask, top, rem, out, k);
+    } else {
+      // Linear or single bins are not key-bit prefixes: select over the whole row again
+      // by radix digits of e from the top, rewriting every output slot (the barrier
+      // orders these stores after the ones above).
+      if (threadIdx.x == 0) sh.n_out = 0;
+      __syncthreads();
+      refine<true>(sh, row, nv, 0ull, 0ull, 64, (uint32_t)k, out, k);
+    }
   }
+}
+
+// When no row can exceed kWide: one launch, workgroup r selects row r with 32 values per
+// thread (no workspace, none of the long-row passes).
+__global__ __launch_bounds__(kThreads) void topk_rows_wide_kernel(Params p) {
+  __shared__ Full sh;
+  const int r = blockIdx.x;
+  const int nv = visible(p, r);
+  if (nv <= p.k) select_trivial_row(p, r, nv);
+  else select_row<kWidePer>(p, r, nv, sh);
 }
 
 // One 8192-element chunk of a long row: element i*kThreads + threadIdx.x of
@@ -520,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
     const int r = blockIdx.x;
     const int nv = visible(p, r);
     if (nv <= p.k) select_trivial_row(p, r, nv);
-    else select_short_row(p, r, nv, sh);
+    else select_row<kPer>(p, r, nv, sh);
     return;
   }
   const int nc = (int)p.meta[kMetaChunks];
@@ -712,7 +742,7 @@ __global__ __launch_bounds__(kThreads) void topk_finish_kernel(Params p) {
     if (item >= nl) {  // uniform
       if (item < nl + ns) {
         const int r = (int)p.short_rows[item - nl];
-        select_short_row(p, r, visible(p, r), sh);
+        select_row<kPer>(p, r, visible(p, r), sh);
         __syncthreads();
       } else {
         const int r = (int)p.triv_rows[item - nl - ns];
@@ -787,7 +817,7 @@ int compute_units() {
 }  // namespace
 
 size_t topk_workspace_bytes(int64_t rows, int32_t max_model_len) {
-  if (max_model_len <= kChunk) return 0;
+  if (max_model_len <= kWide) return 0;
   return layout(rows, max_model_len).total;
 }
 
@@ -803,8 +833,12 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
   p.W = a.token_capacity;
   p.L = a.max_model_len;
   p.k = a.k;
-  if (a.max_model_len <= kChunk) {  // every row fits one workgroup
+  if (a.max_model_len <= kChunk) {  // every row fits one workgroup, 8 values per thread
     hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (a.max_model_len <= kWide) {  // every row fits one workgroup, 32 values per thread
+    hipLaunchKernelGGL(topk_rows_wide_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
   }
   const Layout l = layout(rows, a.max_model_len);

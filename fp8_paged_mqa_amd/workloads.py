@@ -214,6 +214,9 @@ WORKLOADS = {
     "mtp_b32_n2_ctx32k": "MTP verify bs=32 N=2 H=64 ctx~U[2048,32768] L=32768 permuted pool",
     "long_b4_ctx202752": "long context bs=4 N=1 H=64 ctx={65536,131071,131072,202752} L=202752 540k pool, 1% x8 keys",
     "mixed_b128_n4": "mixed serving bs=128 N=4 H=32 ctx~lognormal(6000,1.2) L=202752 interleaved pool",
+    # one GPU's share when the long-context requests are split across 8 GPUs by token
+    # range (each GPU then selects a local top-k that one all-gather merges)
+    "long_b4_cp8_shard": "context-parallel shard: long context bs=4 ctx/8={8192,16384,16384,25344} L=25344 67.5k pool, 1% x8 keys",
 }
 DEFAULT_WORKLOAD = "decode_b64_ctx8192"
 
@@ -251,6 +254,11 @@ def make_named(workload: str, *, poison_unused: bool = True, seed: int | None = 
         return build(name, rng, batch=4, next_n=1, heads=64, ctx=ctx, max_model_len=202752,
                      pool=540_000, table="permuted", table_width=202752, outlier_frac=0.01,
                      poison_unused=poison_unused)
+    if n == 6:
+        ctx = np.array([8192, 16384, 16384, 25344])
+        return build(name, rng, batch=4, next_n=1, heads=64, ctx=ctx, max_model_len=25344,
+                     pool=67_500, table="permuted", table_width=25344, outlier_frac=0.01,
+                     poison_unused=poison_unused)
     if n == 5:
         ctx = np.clip(np.round(np.exp(rng.normal(np.log(6000.0), 1.2, size=128))), 4, 202752)
         ctx = ctx.astype(np.int64)
@@ -275,6 +283,9 @@ def _make_named_blocked(n, rng, name, poison_unused, bs) -> Workload:
     elif n == 4:
         ctx = np.array([65536, 131071, 131072, 202752])
         kw = dict(batch=4, next_n=1, heads=64, max_model_len=202752, rows=540_000, table="permuted")
+    elif n == 6:
+        ctx = np.array([8192, 16384, 16384, 25344])
+        kw = dict(batch=4, next_n=1, heads=64, max_model_len=25344, rows=67_500, table="permuted")
     elif n == 5:
         ctx = np.clip(np.round(np.exp(rng.normal(np.log(6000.0), 1.2, size=128))), 4, 202752).astype(np.int64)
         kw = dict(batch=128, next_n=4, heads=32, max_model_len=202752, rows=int(ctx.sum()), table="interleaved")

@@ -126,7 +126,7 @@ int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* wei
  *   idx             int32  [B*N, k]
  *   workspace       device scratch of at least mqa_topk_workspace_bytes(shape,
  *                   max_model_len, k) bytes, 8-byte aligned (may be NULL when that
- *                   size is 0, i.e. max_model_len <= 8192); contents on entry do not
+ *                   size is 0, i.e. max_model_len <= 32768); contents on entry do not
  *                   matter, the call initialises what it uses, in stream order. Calls
  *                   that overlap in time must not share a workspace.
  * Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED,

@@ -163,8 +163,8 @@ def test_graph_replay_matches_eager():
     import torch
     from fp8_paged_mqa_amd import mqa
     from gpu_helpers import device_inputs, shape_of
-    case = wl.make_case(batch=4, next_n=2, heads=64, ctx=[20000, 9000, 100, 3000],
-                        max_model_len=20000, seed=58)
+    case = wl.make_case(batch=4, next_n=2, heads=64, ctx=[40000, 9000, 100, 3000],
+                        max_model_len=40000, seed=58)
     d = device_inputs(case)
     shape = shape_of(case)
     L, k = case.max_model_len, case.k

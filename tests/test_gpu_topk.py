@@ -1,6 +1,7 @@
 """mqa_topk on crafted logit rows, one call per path (every row fits one workgroup when
-max_model_len <= 8192; longer rows take the chunked path), compared as sets with the
-oracle's selection (larger first, ties by lower position, -0.0 equal to +0.0).
+max_model_len <= 8192, with 8 values per thread, or <= 32768, with 32; longer rows take
+the chunked path), compared as sets with the oracle's selection (larger first, ties by
+lower position, -0.0 equal to +0.0).
 
 The rows are chosen to reach each branch of the selection: spread values (linear bins),
 few distinct values (a threshold bin of thousands of elements, refined by radix digits;
@@ -21,7 +22,7 @@ from gpu_helpers import say
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ["normal", "few", "const", "zeros", "inf", "overflow", "narrow", "wide", "subnormal", "nan"]
+KINDS = ["normal", "few", "const", "zeros", "inf", "overflow", "narrow", "wide", "subnormal", "nan", "two_inf"]
 
 
 def crafted_row(kind, n, rng):
@@ -46,6 +47,10 @@ def crafted_row(kind, n, rng):
         return (rng.choice([-1.0, 1.0], n) * 10.0 ** rng.uniform(-30, 30, n)).astype(np.float32)
     if kind == "subnormal":
         return (rng.integers(-1000, 1000, n) * np.float32(1e-42)).astype(np.float32)
+    if kind == "two_inf":  # key bins (an infinity) holding ~n/2 ties each
+        x = rng.integers(0, 2, n).astype(np.float32)
+        x[rng.integers(0, n)] = np.inf
+        return x
     if kind == "nan":
         x = rng.standard_normal(n).astype(np.float32)
         bits = x.view(np.uint32)
@@ -101,6 +106,16 @@ def test_topk_rows_fit_one_workgroup(k):
     specs = [(kind, nv) for kind in KINDS for nv in nvs if nv <= 8192]
     say(f"[gpu] topk crafted rows L=8192 k={k} rows={len(specs)}")
     run_case(8192, k, specs, seed=7000 + k)
+
+
+@pytest.mark.parametrize("k", [2048, 1, 777])
+def test_topk_wide_rows(k):
+    """Rows up to 32768 in one workgroup each; constant, few-valued and two-valued rows
+    put more than 8192 elements in the threshold bin (the refinement over the row)."""
+    nvs = [1, 2049, 8192, 8193, 20000, 32768]
+    specs = [(kind, nv) for kind in KINDS for nv in nvs]
+    say(f"[gpu] topk crafted rows L=32768 k={k} rows={len(specs)}")
+    run_case(32768, k, specs, seed=7200 + k)
 
 
 @pytest.mark.parametrize("k", [2048, 300])
