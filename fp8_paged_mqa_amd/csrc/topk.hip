@@ -13,34 +13,38 @@
 //
 // Row classes (nv known only on the device):
 //   trivial  nv <= k: every visible position, no logits read.
-//   short    k < nv <= 8192: one workgroup of 1024 threads owns the row, 8 logits per
-//            thread in registers. A block min/max reduction sets 2048 first-level bins
-//            linear in the value (monotone, so bins are ordered like the logits; rows
-//            holding a non-finite value use the top 12 key bits instead). An LDS
-//            histogram and a scan from the top find the bin holding the k-th element
-//            (every wave finishes the search itself after one barrier); everything
-//            above it goes to an LDS output list at slots from one atomic per wave and
-//            the lanes' ranks in the wave's mask, and the threshold bin's elements go
-//            to an LDS candidate list the same way. A small list is finished by
-//            counting, for each candidate, the candidates above it; a large one by
-//            further 11-bit radix digits of e. The output list is then written to the
-//            row in one coalesced pass. One CU per row runs this, so its time is set by
-//            the instructions each wave issues: the path keeps per-element work to a
-//            few vector instructions (buffer loads clamped onto the last visible
-//            element, lane masks from one compare each).
-//   long     nv > 8192: 8192-element chunks. A schedule kernel lists the long rows and
-//            their chunks and clears their histograms; persistent kernels then add each
-//            chunk's 12-bit key histogram into the row's global histogram, emit each
-//            chunk's elements above the threshold bin (one global atomic per workgroup
-//            reserves the output slots) and collect its threshold-bin elements, and
+//   whole    k < nv <= 8192 (8 logits per thread) or <= 32768 (32 per thread): one
+//            workgroup of 1024 threads owns the row, its logits in registers. A block
+//            min/max reduction sets 2048 first-level bins linear in the value (monotone,
+//            so bins are ordered like the logits; rows holding a non-finite value use the
+//            top 12 key bits instead, constant rows a single bin). An LDS histogram and a
+//            scan from the top find the bin holding the k-th element (every wave finishes
+//            the search itself after one barrier). Each wave counts its elements above
+//            that bin and in it and publishes the counts; after one barrier it takes its
+//            first slots from a prefix over the 16 counts and each lane its rank in the
+//            wave's ballot mask: positions above the bin go straight to the output row,
+//            the bin's own elements to an LDS candidate list. A small list is finished by
+//            counting, for each candidate, the candidates above it (the count is the
+//            slot); a large one by further 11-bit radix digits of e, or over the whole
+//            row if the bin holds more than the list (kCap). One CU serves a row, so the
+//            time is set by the instructions each wave issues: per-element work is kept
+//            to a few vector instructions (buffer loads clamped onto the last visible
+//            element, lane masks from one compare each, emission by mask rank).
+//   long     nv > 8192 when max_model_len > 32768: 8192-element chunks. A
+//            schedule kernel lists the rows of each class and the long rows' chunks and
+//            clears their histograms; persistent kernels then add each chunk's 12-bit key
+//            histogram into the row's global histogram (the next chunk's loads in flight
+//            meanwhile), emit each chunk's elements above the threshold bin (slots from
+//            one pair of global atomics per workgroup, a prefix over the waves' counts
+//            and the lanes' ballot ranks) and collect its threshold-bin elements, and
 //            finish each row's candidates in LDS. If the threshold bin holds more than
 //            kCap elements (extreme ties, e.g. a constant row) the finish refines over
-//            the whole row from global memory: slower, same result. The short and
-//            trivial rows of such a call are selected by the finishing pass's spare
-//            workgroups.
-// When max_model_len <= 8192 no row can be long: one launch, one workgroup per row. Up to
-// 32768 the same holds with 32 logits per thread (a threshold bin of more than kCap
-// elements then refines over the row itself); only longer rows take the chunked passes.
+//            the whole row from global memory: slower, same result. The finishing pass's
+//            spare workgroups select the call's rows of at most 8192 and the trivial rows
+//            (selecting rows up to 32768 whole there was slower: the wide select in the
+//            same kernel costs its other paths, and the rows queue behind other items).
+// When max_model_len <= 8192 (8 per thread) or <= 32768 (32 per thread) no row is long:
+// one launch, one workgroup per row, no workspace.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
