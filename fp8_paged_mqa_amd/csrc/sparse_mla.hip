@@ -92,11 +92,9 @@ struct Smem {
   uint8_t tile[kNBuf][kTileBytes];
   float s[kH * kSStride];        // scores of the tile, [head][token]
   float wmax[kWaves][kH];
-  int32_t rows[kMaxTiles][kTile];  // row to load for each token of each live tile
+  int32_t rows[kMaxTiles][kTile];  // row to load for each token of each list tile
   uint64_t padm[kMaxTiles];        // bit u: token u of the tile is padding
   uint64_t badm[kMaxTiles];        // bit u: token u names a position outside the cache
-  int32_t live[kMaxTiles];         // list tile of each live tile
-  int32_t nlive;
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -197,7 +195,19 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
   const int e0 = split * p.tps * kTile;
   const int ntiles = min(p.tps, (p.topk - e0 + kTile - 1) / kTile);
 
-  // Query rows as B operands of S^T = K Q^T: lane (G, i) holds dims [32s + 8G, +8) of
+  // Resolve every listed position of this split to a cache row. Wave w takes list tiles
+  // w and w+4: both index loads, then both table loads, so two round trips in all.
+  static_assert(kMaxTiles == 2 * kWaves, "two list tiles per wave");
+  const uint32_t cap = (uint32_t)p.W << p.bshift;
+  const int smask = (1 << p.bshift) - 1;
+  int pos[2], ent[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = e0 + (wave + kWaves * h) * kTile + lane;
+    pos[h] = (wave + kWaves * h < ntiles && e < p.topk) ? p.idx[(int64_t)r * p.topk + e] : -1;
+  }
+  // Query rows, loaded behind the index loads (so the table lookups wait for the indices
+  // only), as B operands of S^T = K Q^T: lane (G, i) holds dims [32s + 8G, +8) of
   // head i for the 18 k-steps s.
   f16x8 qb[kD / 32];
   {
@@ -210,17 +220,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
     }
   }
 
-  // Resolve every listed position of this split to a cache row. Wave w takes list tiles
-  // w and w+4: both index loads, then both table loads, so two round trips in all.
-  static_assert(kMaxTiles == 2 * kWaves, "two list tiles per wave");
-  const uint32_t cap = (uint32_t)p.W << p.bshift;
-  const int smask = (1 << p.bshift) - 1;
-  int pos[2], ent[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = e0 + (wave + kWaves * h) * kTile + lane;
-    pos[h] = (wave + kWaves * h < ntiles && e < p.topk) ? p.idx[(int64_t)r * p.topk + e] : -1;
-  }
 #pragma unroll
   for (int h = 0; h < 2; ++h)
     ent[h] = (pos[h] >= 0 && (uint32_t)pos[h] < cap) ? p.bt[(int64_t)b * p.W + (pos[h] >> p.bshift)] : -1;
@@ -244,46 +243,23 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {  // live tiles: not all padding
-    int n = 0;
-    for (int t = 0; t < ntiles; ++t)
-      if (sm.padm[t] != ~0ull) sm.live[n++] = t;
-    sm.nlive = n;
-  }
-  __syncthreads();
-  const int nlive = uniform(sm.nlive);
-  // Compact the live tiles to the front (in place: live[k] >= k).
-  int myrow[kMaxTiles];
-  uint64_t mypad[kMaxTiles], mybad[kMaxTiles];
-#pragma unroll
-  for (int k = 0; k < kMaxTiles; ++k) {
-    if (k < nlive) {
-      const int t = sm.live[k];
-      myrow[k] = sm.rows[t][lane];
-      mypad[k] = sm.padm[t];
-      mybad[k] = sm.badm[t];
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int k = 0; k < kMaxTiles; ++k)
-      if (k < nlive) {
-        sm.rows[k][lane] = myrow[k];
-        if (lane == 0) {
-          sm.padm[k] = mypad[k];
-          sm.badm[k] = mybad[k];
-        }
-      }
-  }
-  __syncthreads();
+  // Live tiles (not all padding): every wave takes the list from one ballot over the
+  // tiles' padding masks and keeps it in scalar registers; the loop reaches a live tile's
+  // resolved rows through it, so nothing is moved.
+  const uint64_t livem = __ballot(lane < ntiles && sm.padm[lane < kMaxTiles ? lane : 0] != ~0ull);
+  const int nlive = __popcll(livem);
+  auto live_tile = [&](int k) {  // list tile of the k-th live tile
+    uint64_t m = livem;
+    for (int j = 0; j < k; ++j) m &= m - 1;
+    return (int)__builtin_ctzll(m);
+  };
 
   // The query conversion (and its waits on the query loads) must not sink below the
   // prefetch: a wait on a query load would then also wait for the tiles behind it.
 #pragma unroll
   for (int s = 0; s < kD / 32; ++s) asm volatile("" ::"v"(qb[s]));
   // Prefetch: live tiles 0..2.
-  for (int k = 0; k < min(nlive, kNBuf - 1); ++k) issue_tile(p, sm, k, k, wave, lane);
+  for (int k = 0; k < min(nlive, kNBuf - 1); ++k) issue_tile(p, sm, live_tile(k), k, wave, lane);
 
   f32x4 o[8];
 #pragma unroll
@@ -298,13 +274,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
     else if (ahead == 1) wait_vm<kLoads>();
     else wait_vm<0>();
     barrier();  // tile k is in LDS, and every wave is done with tile k-1
-    if (k + kNBuf - 1 < nlive) issue_tile(p, sm, k + kNBuf - 1, (k + kNBuf - 1) & (kNBuf - 1), wave, lane);
+    if (k + kNBuf - 1 < nlive) issue_tile(p, sm, live_tile(k + kNBuf - 1), (k + kNBuf - 1) & (kNBuf - 1), wave, lane);
     const uint8_t* const tb = sm.tile[buf];
 
-    const uint64_t padm = ((uint64_t)(uint32_t)uniform((int)(uint32_t)sm.padm[k])) |
-                          ((uint64_t)(uint32_t)uniform((int)(uint32_t)(sm.padm[k] >> 32)) << 32);
-    const uint64_t badm = ((uint64_t)(uint32_t)uniform((int)(uint32_t)sm.badm[k])) |
-                          ((uint64_t)(uint32_t)uniform((int)(uint32_t)(sm.badm[k] >> 32)) << 32);
+    const int tk = live_tile(k);
+    const uint64_t padm = ((uint64_t)(uint32_t)uniform((int)(uint32_t)sm.padm[tk])) |
+                          ((uint64_t)(uint32_t)uniform((int)(uint32_t)(sm.padm[tk] >> 32)) << 32);
+    const uint64_t badm = ((uint64_t)(uint32_t)uniform((int)(uint32_t)sm.badm[tk])) |
+                          ((uint64_t)(uint32_t)uniform((int)(uint32_t)(sm.badm[tk] >> 32)) << 32);
 
     // Every LDS read of the tile first: the key operands of the scores (lane (G, i): dims
     // [32s + 8G, +8) of token 16*wave + i) and the value operands (transposed reads,
