@@ -15,8 +15,8 @@
 //     converted exactly to f16 (v_cvt_scalef32_pk_f16_fp8, scale 1) and contracted with
 //     v_mfma_f32_16x16x32_f16, four chained per 128-wide row: f16 products of e4m3
 //     values are exact and the fp32 accumulation is correctly rounded.
-//   * Schedule: one round of persistent workgroups (CUs x occupancy), so no workgroup
-//     waits for a slot. Each workgroup scans context_lens into LDS prefix sums (DPP wave
+//   * Schedule: one round of persistent workgroups (one per CU), so no workgroup waits
+//     for a slot. Each workgroup scans context_lens into LDS prefix sums (DPP wave
 //     scans, one barrier); every
 //     wave then takes an equal contiguous share of all 64-token key stages of all
 //     requests (split at request boundaries into segments), and afterwards an equal
@@ -507,18 +507,18 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   p.vec_store = (a.max_model_len % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
   KernelFn fn = kTable[tpj - 1][jpg - 1];
   const size_t lds = logits_lds_bytes(a.batch);
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, lds) !=
-          hipSuccess || per_cu < 1)
-    per_cu = 1;
-  // One round of persistent workgroups, but no more waves than there can be work for:
-  // the host knows an upper bound of the key stages (every request at its largest
-  // context) and of the tail chunks, and small calls then launch a small grid.
+  // One round of persistent workgroups, one per CU, but no more waves than there can be
+  // work for: the host knows an upper bound of the key stages (every request at its
+  // largest context) and of the tail chunks, and small calls then launch a small grid.
+  // Four waves per CU measured faster than eight (two workgroups): each wave takes twice
+  // the stages and pays the start-up - schedule, table and query loads queued behind the
+  // other waves' gathers - half as often. Two waves per CU, or a deeper prefetch (three or
+  // four stages in flight per wave), were slower.
   const int64_t ctx_cap = a.max_model_len < (int64_t)p.Wt ? a.max_model_len : (int64_t)p.Wt;
   const int64_t stage_bound = (int64_t)a.batch * ((ctx_cap + kStage - 1) / kStage) * p.groups;
   const int64_t tail_bound = (int64_t)a.batch * a.next_n * ((a.max_model_len + kTailChunk - 1) / kTailChunk);
   const int64_t need = (std::max(stage_bound, tail_bound) + kWavesPerGroup - 1) / kWavesPerGroup;
-  const int64_t full = (int64_t)compute_units() * per_cu;
+  const int64_t full = (int64_t)compute_units();
   const int blocks = (int)std::max<int64_t>(1, std::min(full, need));
   hipLaunchKernelGGL(fn, dim3(blocks), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
