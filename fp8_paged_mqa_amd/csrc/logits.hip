@@ -510,15 +510,20 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   // One round of persistent workgroups, one per CU, but no more waves than there can be
   // work for: the host knows an upper bound of the key stages (every request at its
   // largest context) and of the tail chunks, and small calls then launch a small grid.
-  // Four waves per CU measured faster than eight (two workgroups): each wave takes twice
-  // the stages and pays the start-up - schedule, table and query loads queued behind the
-  // other waves' gathers - half as often. Two waves per CU, or a deeper prefetch (three or
-  // four stages in flight per wave), were slower.
+  // Four waves per CU measured faster than eight (two workgroups) on single-token pages
+  // and on single-group calls: each wave takes twice the stages and pays the start-up -
+  // schedule, table and query loads queued behind the other waves' gathers - half as
+  // often. With 64-token pages and several query groups per request (every key stage read
+  // once per group, the later reads mostly from L2) eight waves per CU were faster (4 to
+  // 10%): the key reads are whole lines and the wave is waiting on latency, not on HBM.
+  // Two waves per CU, or a deeper prefetch (three or four stages in flight per wave), were
+  // slower everywhere.
   const int64_t ctx_cap = a.max_model_len < (int64_t)p.Wt ? a.max_model_len : (int64_t)p.Wt;
   const int64_t stage_bound = (int64_t)a.batch * ((ctx_cap + kStage - 1) / kStage) * p.groups;
   const int64_t tail_bound = (int64_t)a.batch * a.next_n * ((a.max_model_len + kTailChunk - 1) / kTailChunk);
   const int64_t need = (std::max(stage_bound, tail_bound) + kWavesPerGroup - 1) / kWavesPerGroup;
-  const int64_t full = (int64_t)compute_units();
+  const int64_t per_cu = (a.block_shift >= 6 && p.groups > 1 && tpj * jpg <= 4) ? 2 : 1;
+  const int64_t full = per_cu * compute_units();
   const int blocks = (int)std::max<int64_t>(1, std::min(full, need));
   hipLaunchKernelGGL(fn, dim3(blocks), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
