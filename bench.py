@@ -283,7 +283,7 @@ def main():
                     help="size of the plain device copy run once for counter calibration (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
     if args.op == "kwrite":

@@ -18,9 +18,11 @@
 //   * Schedule: one round of persistent workgroups (one per CU), so no workgroup waits
 //     for a slot. Each workgroup scans context_lens into LDS prefix sums (DPP wave
 //     scans, one barrier); every
-//     wave then takes an equal contiguous share of all 64-token key stages of all
-//     requests (split at request boundaries into segments), and afterwards an equal
-//     share of the 1 KB chunks of -inf tail that lie past each request's last stage.
+//     wave then takes an equal contiguous share of the work units of all requests -
+//     each 64-token key stage one unit, and each request's start one more, the cost of
+//     loading another request's table entries and query rows - split at request
+//     boundaries into segments, and afterwards an equal share of the 1 KB chunks of
+//     -inf tail that lie past each request's last stage.
 //     The balance does not depend on how context lengths are distributed, and nothing
 //     is read from the device by the host.
 //   * One wave owns a group of decode rows (at most 4 MFMA row tiles of 16 heads, so at
@@ -76,6 +78,10 @@ constexpr int kThreads = kWave * kWavesPerGroup;
 constexpr int kStage = 64;       // tokens per pipeline stage = 4 MFMA column tiles
 constexpr int kTilesPerStage = kStage / 16;
 constexpr int kTailChunk = 4 * kWave;  // floats per tail chunk: one float4 per lane
+// Work units a request's start costs on top of its stages when the key stages are shared
+// out: a wave whose share enters another request loads that request's table entries and
+// query rows before its next gathers, which measured about one stage of time.
+constexpr int kStartUnits = 1;
 
 struct Params {
   const uint8_t* q;
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   extern __shared__ int lds[];
   const int B = p.B;
   int* ctx_s = lds;                     // [B]
-  int* stage_pref = lds + B;            // [B+1]
+  int* stage_pref = lds + B;            // [B+1] work units: stages + kStartUnits each
   int* tail_pref = stage_pref + B + 1;  // [B+1]
   int* scan_tmp = tail_pref + B + 1;    // [2 * kWavesPerGroup]
 
@@ -217,10 +223,11 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         const int ns = (ctx + kStage - 1) / kStage;
         const int tail0 = ns * kStage;
         const int nc = tail0 < L ? p.N * ((L - tail0 + kTailChunk - 1) / kTailChunk) : 0;
+        const int nu = ns > 0 ? ns + kStartUnits : 0;
         ctx_s[b] = ctx;
-        stage_pref[b] = ns;  // counts for now
+        stage_pref[b] = nu;  // counts for now
         tail_pref[b] = nc;
-        stages += ns;
+        stages += nu;
         chunks += nc;
       }
     }
@@ -230,10 +237,10 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
     for (int i = 0; i < per; ++i) {
       const int b = r0 + i;
       if (b < B) {
-        const int ns = stage_pref[b], nc = tail_pref[b];
+        const int nu = stage_pref[b], nc = tail_pref[b];
         stage_pref[b] = s_run;
         tail_pref[b] = c_run;
-        s_run += ns;
+        s_run += nu;
         c_run += nc;
       }
     }
@@ -262,142 +269,145 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
     const uint8_t* kv_g = p.kv + 16 * g;  // this lane's first key slice
     const uint8_t* kv_s = p.kv + kD;      // scales
     while (lo < hi) {
-      // Segment: stages [s0, s0 + nstage) of request b.
+      // Segment: stages [s0, s0 + nstage) of request b, the stages whose units fall in
+      // [lo, seg_hi); none when the share holds only the request's start units.
       const int seg_hi = min(hi, stage_pref[b + 1]);
-      const int s0 = lo - stage_pref[b];
-      const int nstage = seg_hi - lo;
-      const int ctx = ctx_s[b];
-      const int t0 = s0 * kStage;
-      const int t_end = min((s0 + nstage) * kStage, L);
-      const int t_need = min(t_end, ctx);
-      float* const out0 = p.out + (int64_t)(b * p.N + j0) * L;
+      const int s0 = max(lo - stage_pref[b] - kStartUnits, 0);
+      const int nstage = seg_hi - stage_pref[b] - kStartUnits - s0;
+      if (nstage > 0) {
+        const int ctx = ctx_s[b];
+        const int t0 = s0 * kStage;
+        const int t_end = min((s0 + nstage) * kStage, L);
+        const int t_need = min(t_end, ctx);
+        float* const out0 = p.out + (int64_t)(b * p.N + j0) * L;
 
-      int nv[JPG];  // visible positions of each owned decode row
+        int nv[JPG];  // visible positions of each owned decode row
 #pragma unroll
-      for (int jl = 0; jl < JPG; ++jl) nv[jl] = min(ctx - p.N + (j0 + jl) + 1, L);
+        for (int jl = 0; jl < JPG; ++jl) nv[jl] = min(ctx - p.N + (j0 + jl) + 1, L);
 
-      const int32_t* btb = p.bt + (int64_t)b * p.W;
-      const int wmax = p.W - 1;
-      auto load_table = [&](int st) -> int {
-        return btb[st < nstage ? min((t0 + st * kStage + lane) >> p.bshift, wmax) : 0];
-      };
-      // Table entries of the first two stages first: the gathers wait for them, and a
-      // wait on a load also waits for every load issued before it.
-      int tab0 = load_table(0);
-      int tab1 = load_table(1);
-      __builtin_amdgcn_sched_barrier(0);
-      // Query rows of this segment: raw bytes now, f16 A operands once the first key
-      // gathers are on their way (the conversion then overlaps their latency).
-      i32x4 qraw[TILES][2];
-      f32x4 wv[TILES];
-      {
-        const uint8_t* qb = p.q + ((int64_t)b * p.N + j0) * p.H * kD;
-        const float* wb = p.w + ((int64_t)b * p.N + j0) * p.H;
-#pragma unroll
-        for (int m = 0; m < TILES; ++m) {
-          // Row tiles of decode rows past N repeat the last row (never stored).
-          const int mr = min(m / TPJ, jn - 1) * TPJ + m % TPJ;
-          const uint8_t* qr = qb + (mr * 16 + c) * kD;
-          qraw[m][0] = load16(qr + 16 * g);
-          qraw[m][1] = load16(qr + 64 + 16 * g);
-          wv[m] = *reinterpret_cast<const f32x4*>(wb + mr * 16 + 4 * g);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      Operand qa[TILES];
-
-      auto issue_keys = [&](int st, int tab, Stage& s) {
-        const bool live = st < nstage;  // wave-uniform
-        int ph[kTilesPerStage];
-#pragma unroll
-        for (int u = 0; u < kTilesPerStage; ++u) ph[u] = __shfl(tab, u * 16 + c);
-        const uint32_t smask = (1u << p.bshift) - 1u;  // slot of a token in its block
-        const uint32_t tok = (uint32_t)(t0 + st * kStage + c);
-#pragma unroll
-        for (int u = 0; u < kTilesPerStage; ++u) {
-          const uint32_t slot = (tok + 16u * u) & smask;
-          const uint32_t row = (live && (uint32_t)ph[u] < p.nblk) ? ((uint32_t)ph[u] << p.bshift) | slot : 0u;
-          const uint8_t* kp = kv_g + (uint64_t)row * kRow;
-          s.phys[u] = ph[u];
-          s.lo[u] = load16(kp);
-          s.hi[u] = load16(kp + 64);
-          s.scale[u] = *reinterpret_cast<const float*>(kv_s + (uint64_t)row * kRow);
-        }
-      };
-
-      auto compute_store = [&](int st, const Stage& s) {
-        const int tc = t0 + st * kStage;
-        float keep[JPG];
-#pragma unroll
-        for (int jl = 0; jl < JPG; ++jl) keep[jl] = 0.0f;
-#pragma unroll
-        for (int u = 0; u < kTilesPerStage; ++u) {
-          const int t = tc + u * 16 + c;
-          const bool in_ctx = t < t_need;
-          const bool ok = in_ctx && (uint32_t)s.phys[u] < p.nblk;
-          // Past ctx the column is masked below; a bad table entry poisons it with NaN.
-          const float sc = ok ? s.scale[u] : (in_ctx ? __builtin_nanf("") : 0.0f);
-          i32x4 lo = s.lo[u], hi = s.hi[u];
-          if (__ballot(__float_as_int(sc) < 0) != 0) {  // wave-uniform: rare
-            const int flip = (__float_as_int(sc) < 0) ? (int)0x80808080 : 0;
-            lo ^= flip;
-            hi ^= flip;
-          }
-          const Operand kb = to_operand(lo, hi);
-          const float sabs = __builtin_fabsf(sc);
-          f32x4 acc[TILES];
+        const int32_t* btb = p.bt + (int64_t)b * p.W;
+        const int wmax = p.W - 1;
+        auto load_table = [&](int st) -> int {
+          return btb[st < nstage ? min((t0 + st * kStage + lane) >> p.bshift, wmax) : 0];
+        };
+        // Table entries of the first two stages first: the gathers wait for them, and a
+        // wait on a load also waits for every load issued before it.
+        int tab0 = load_table(0);
+        int tab1 = load_table(1);
+        __builtin_amdgcn_sched_barrier(0);
+        // Query rows of this segment: raw bytes now, f16 A operands once the first key
+        // gathers are on their way (the conversion then overlaps their latency).
+        i32x4 qraw[TILES][2];
+        f32x4 wv[TILES];
+        {
+          const uint8_t* qb = p.q + ((int64_t)b * p.N + j0) * p.H * kD;
+          const float* wb = p.w + ((int64_t)b * p.N + j0) * p.H;
 #pragma unroll
           for (int m = 0; m < TILES; ++m) {
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[0], kb.k[0], f32x4{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-            for (int k = 1; k < 4; ++k)
-              acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[k], kb.k[k], acc[m], 0, 0, 0);
-          }
-#pragma unroll
-          for (int jl = 0; jl < JPG; ++jl) {
-            float part = 0.0f;
-#pragma unroll
-            for (int mm = 0; mm < TPJ; ++mm) {
-              const int m = jl * TPJ + mm;
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                part = __builtin_fmaf(wv[m][v], __builtin_elementwise_maximum(acc[m][v], 0.0f), part);
-            }
-            part = sum_lane_groups(part);
-            if (g == u) keep[jl] = part * sabs;
+            // Row tiles of decode rows past N repeat the last row (never stored).
+            const int mr = min(m / TPJ, jn - 1) * TPJ + m % TPJ;
+            const uint8_t* qr = qb + (mr * 16 + c) * kD;
+            qraw[m][0] = load16(qr + 16 * g);
+            qraw[m][1] = load16(qr + 64 + 16 * g);
+            wv[m] = *reinterpret_cast<const f32x4*>(wb + mr * 16 + 4 * g);
           }
         }
-        const int t = tc + lane;  // lane (g, c) stores token 16g + c of the stage
-        if (t < t_end) {
-#pragma unroll
-          for (int jl = 0; jl < JPG; ++jl)
-            if (jl < jn) out0[(int64_t)jl * L + t] = (t < nv[jl]) ? keep[jl] : -__builtin_inff();
-        }
-      };
+        __builtin_amdgcn_sched_barrier(0);
+        Operand qa[TILES];
 
-      // Software pipeline: keys of two stages in flight, table entries two stages ahead
-      // of their use; the compute of stage s waits only for stage s's loads, and its
-      // registers are refilled with stage s+2 right after.
-      // The prologue issues in the loop's order (keys of a stage, then the table entries
-      // two stages on), so the wait counts computed for the loop's first pass hold for
-      // every pass; stages past the segment issue harmless loads of row 0, so the loop
-      // body is straight-line code. sched_barrier(0) keeps the scheduler from pulling a
-      // use of a load up next to it, which would serialise the latencies.
-      Stage sa, sb;
-      issue_keys(0, tab0, sa);
-      tab0 = load_table(2);
-      issue_keys(1, tab1, sb);
-      tab1 = load_table(3);
-      __builtin_amdgcn_sched_barrier(0);
+        auto issue_keys = [&](int st, int tab, Stage& s) {
+          const bool live = st < nstage;  // wave-uniform
+          int ph[kTilesPerStage];
 #pragma unroll
-      for (int m = 0; m < TILES; ++m) qa[m] = to_operand(qraw[m][0], qraw[m][1]);
-      for (int st = 0; st < nstage; st += 2) {
-        compute_store(st, sa);
-        issue_keys(st + 2, tab0, sa);
-        tab0 = load_table(st + 4);
-        if (st + 1 < nstage) compute_store(st + 1, sb);
-        issue_keys(st + 3, tab1, sb);
-        tab1 = load_table(st + 5);
+          for (int u = 0; u < kTilesPerStage; ++u) ph[u] = __shfl(tab, u * 16 + c);
+          const uint32_t smask = (1u << p.bshift) - 1u;  // slot of a token in its block
+          const uint32_t tok = (uint32_t)(t0 + st * kStage + c);
+#pragma unroll
+          for (int u = 0; u < kTilesPerStage; ++u) {
+            const uint32_t slot = (tok + 16u * u) & smask;
+            const uint32_t row = (live && (uint32_t)ph[u] < p.nblk) ? ((uint32_t)ph[u] << p.bshift) | slot : 0u;
+            const uint8_t* kp = kv_g + (uint64_t)row * kRow;
+            s.phys[u] = ph[u];
+            s.lo[u] = load16(kp);
+            s.hi[u] = load16(kp + 64);
+            s.scale[u] = *reinterpret_cast<const float*>(kv_s + (uint64_t)row * kRow);
+          }
+        };
+
+        auto compute_store = [&](int st, const Stage& s) {
+          const int tc = t0 + st * kStage;
+          float keep[JPG];
+#pragma unroll
+          for (int jl = 0; jl < JPG; ++jl) keep[jl] = 0.0f;
+#pragma unroll
+          for (int u = 0; u < kTilesPerStage; ++u) {
+            const int t = tc + u * 16 + c;
+            const bool in_ctx = t < t_need;
+            const bool ok = in_ctx && (uint32_t)s.phys[u] < p.nblk;
+            // Past ctx the column is masked below; a bad table entry poisons it with NaN.
+            const float sc = ok ? s.scale[u] : (in_ctx ? __builtin_nanf("") : 0.0f);
+            i32x4 lo = s.lo[u], hi = s.hi[u];
+            if (__ballot(__float_as_int(sc) < 0) != 0) {  // wave-uniform: rare
+              const int flip = (__float_as_int(sc) < 0) ? (int)0x80808080 : 0;
+              lo ^= flip;
+              hi ^= flip;
+            }
+            const Operand kb = to_operand(lo, hi);
+            const float sabs = __builtin_fabsf(sc);
+            f32x4 acc[TILES];
+#pragma unroll
+            for (int m = 0; m < TILES; ++m) {
+              acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[0], kb.k[0], f32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+              for (int k = 1; k < 4; ++k)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[k], kb.k[k], acc[m], 0, 0, 0);
+            }
+#pragma unroll
+            for (int jl = 0; jl < JPG; ++jl) {
+              float part = 0.0f;
+#pragma unroll
+              for (int mm = 0; mm < TPJ; ++mm) {
+                const int m = jl * TPJ + mm;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                  part = __builtin_fmaf(wv[m][v], __builtin_elementwise_maximum(acc[m][v], 0.0f), part);
+              }
+              part = sum_lane_groups(part);
+              if (g == u) keep[jl] = part * sabs;
+            }
+          }
+          const int t = tc + lane;  // lane (g, c) stores token 16g + c of the stage
+          if (t < t_end) {
+#pragma unroll
+            for (int jl = 0; jl < JPG; ++jl)
+              if (jl < jn) out0[(int64_t)jl * L + t] = (t < nv[jl]) ? keep[jl] : -__builtin_inff();
+          }
+        };
+
+        // Software pipeline: keys of two stages in flight, table entries two stages ahead
+        // of their use; the compute of stage s waits only for stage s's loads, and its
+        // registers are refilled with stage s+2 right after.
+        // The prologue issues in the loop's order (keys of a stage, then the table entries
+        // two stages on), so the wait counts computed for the loop's first pass hold for
+        // every pass; stages past the segment issue harmless loads of row 0, so the loop
+        // body is straight-line code. sched_barrier(0) keeps the scheduler from pulling a
+        // use of a load up next to it, which would serialise the latencies.
+        Stage sa, sb;
+        issue_keys(0, tab0, sa);
+        tab0 = load_table(2);
+        issue_keys(1, tab1, sb);
+        tab1 = load_table(3);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < TILES; ++m) qa[m] = to_operand(qraw[m][0], qraw[m][1]);
+        for (int st = 0; st < nstage; st += 2) {
+          compute_store(st, sa);
+          issue_keys(st + 2, tab0, sa);
+          tab0 = load_table(st + 4);
+          if (st + 1 < nstage) compute_store(st + 1, sb);
+          issue_keys(st + 3, tab1, sb);
+          tab1 = load_table(st + 5);
+        }
       }
 
       lo = seg_hi;
@@ -519,7 +529,7 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   // Two waves per CU, or a deeper prefetch (three or four stages in flight per wave), were
   // slower everywhere.
   const int64_t ctx_cap = a.max_model_len < (int64_t)p.Wt ? a.max_model_len : (int64_t)p.Wt;
-  const int64_t stage_bound = (int64_t)a.batch * ((ctx_cap + kStage - 1) / kStage) * p.groups;
+  const int64_t stage_bound = (int64_t)a.batch * ((ctx_cap + kStage - 1) / kStage + kStartUnits) * p.groups;
   const int64_t tail_bound = (int64_t)a.batch * a.next_n * ((a.max_model_len + kTailChunk - 1) / kTailChunk);
   const int64_t need = (std::max(stage_bound, tail_bound) + kWavesPerGroup - 1) / kWavesPerGroup;
   const int64_t per_cu = (a.block_shift >= 6 && p.groups > 1 && tpj * jpg <= 4) ? 2 : 1;
