@@ -70,7 +70,7 @@ const char* mqa_status_string(int status) {
       return "unsupported: needs head_dim 128, block_size a power of two up to 65536 (with "
              "block_table_stride * block_size and, for block_size > 1, num_blocks * block_size "
              "below 2^31), heads a multiple of 16 up to 128, "
-             "next_n 1..4, max_model_len <= 2^30, batch <= 8192 for the logits, k 1..2048, non-paged n <= 2^29, 16-byte aligned q and weights, "
+             "next_n 1..4, max_model_len <= 2^30, batch <= 8192 and batch * next_n * (ceil(max_model_len / 64) + 1) < 2^31 for the logits, k 1..2048, non-paged n <= 2^29, 16-byte aligned q and weights, "
              "4-byte aligned kv_cache, logits, idx and integer arrays; sparse MLA decode: heads 16, "
              "head_dim 576, v_dim 512, rows <= 65535, topk <= 2^20, 16-byte aligned q, kv_cache, out and workspace";
     case MQA_ERR_WORKSPACE: return "workspace missing or too small";
@@ -86,6 +86,10 @@ int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* wei
   const int st = check_shape(shape, max_model_len);
   if (st != MQA_OK) return st;
   if (shape->batch > kMaxBatch) return MQA_ERR_UNSUPPORTED;
+  // The kernel counts key stages (64 tokens, plus one unit per request) and -inf tail
+  // chunks in 32-bit prefix sums.
+  if ((int64_t)shape->batch * shape->next_n * ((max_model_len + 63) / 64 + 1) > INT32_MAX)
+    return MQA_ERR_UNSUPPORTED;
   if (shape->batch == 0) return MQA_OK;
   if (!q || !kv_cache || !weights || !context_lens || !block_tables || !out) return MQA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(weights, 16) || !aligned(kv_cache, 4) || !aligned(out, 4) ||

@@ -94,7 +94,9 @@ typedef struct mqa_shape {
  *   weights         float  [B*N, H]
  *   context_lens    int32  [B]
  *   block_tables    int32  [B, W]
- *   max_model_len   L >= 1, the length of each output row
+ *   max_model_len   L >= 1, the length of each output row; B * N * (ceil(L/64) + 1)
+ *                   must stay below 2^31 (the work is counted in 32-bit units), else
+ *                   MQA_ERR_UNSUPPORTED
  *   out             float  [B*N, L]         every element is written
  *   shape, stream   see above
  * Accuracy: fp8 x fp8 products are exact, accumulated in fp32; relu, weight and head

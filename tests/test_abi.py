@@ -113,6 +113,12 @@ def test_logits_batch_limit():
     assert call_topk(good_shape(batch=8193)) != mqa.MQA_ERR_UNSUPPORTED
 
 
+def test_logits_work_count_limit():
+    # stages and -inf chunks are counted in 32 bits: B * N * (ceil(L / 64) + 1) < 2^31
+    assert call_logits(good_shape(batch=8192, next_n=4), L=1 << 30) == mqa.MQA_ERR_UNSUPPORTED
+    assert call_logits(good_shape(batch=1024, next_n=4), L=1 << 25) == mqa.MQA_ERR_UNSUPPORTED  # 4096 * (2^19 + 1)
+
+
 def test_topk_k_range():
     assert call_topk(good_shape(), k=0) == mqa.MQA_ERR_SHAPE
     assert call_topk(good_shape(), k=2049) == mqa.MQA_ERR_UNSUPPORTED
