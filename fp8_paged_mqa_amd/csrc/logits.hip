@@ -262,10 +262,21 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   const int j0 = group * JPG;         // first decode row of this wave
   const int jn = min(JPG, p.N - j0);  // decode rows this wave owns
   if (wi < nw) {
+    // Share [floor(wi*S/nw), floor((wi+1)*S/nw)) in 32-bit arithmetic: with S = sq*nw + sr,
+    // floor(wi*S/nw) = wi*sq + floor(wi*sr/nw), and wi*sr < nw^2 fits.
     const int S = stage_pref[B];
-    int lo = (int)((int64_t)wi * S / nw);
-    const int hi = (int)((int64_t)(wi + 1) * S / nw);
-    int b = lo < hi ? locate(stage_pref, B, lo) : 0;
+    const int sq = S / nw, sr = S - sq * nw;
+    int lo = wi * sq + (wi * sr) / nw;
+    const int hi = (wi + 1) * sq + ((wi + 1) * sr) / nw;
+    int b = 0;
+    if (lo < hi) {
+      if (B <= kWave) {  // the prefix entries <= lo are a run from entry 0: count them
+        const uint64_t le = __ballot(lane < B && stage_pref[lane < B ? lane : 0] <= lo);
+        b = __popcll(le) - 1;
+      } else {
+        b = locate(stage_pref, B, lo);
+      }
+    }
     const uint8_t* kv_g = p.kv + 16 * g;  // this lane's first key slice
     const uint8_t* kv_s = p.kv + kD;      // scales
     while (lo < hi) {
