@@ -82,6 +82,9 @@ constexpr int kTailChunk = 4 * kWave;  // floats per tail chunk: one float4 per 
 // out: a wave whose share enters another request loads that request's table entries and
 // query rows before its next gathers, which measured about one stage of time.
 constexpr int kStartUnits = 1;
+// Tail chunks one key stage is counted as when the -inf tail is shared out (a stage
+// gathers ~17 KB of cache lines, a chunk stores 1 KB; 4, 8 and 16 measured alike).
+constexpr int kStageChunks = 8;
 
 struct Params {
   const uint8_t* q;
@@ -261,11 +264,12 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   const int nw = nwaves / G;
   const int j0 = group * JPG;         // first decode row of this wave
   const int jn = min(JPG, p.N - j0);  // decode rows this wave owns
+  // Share [floor(wi*S/nw), floor((wi+1)*S/nw)) in 32-bit arithmetic: with S = sq*nw + sr,
+  // floor(wi*S/nw) = wi*sq + floor(wi*sr/nw), and wi*sr < nw^2 fits. sr waves of each
+  // group take sq + 1 units, the others sq.
+  const int S = stage_pref[B];
+  const int sq = S / nw, sr = S - sq * nw;
   if (wi < nw) {
-    // Share [floor(wi*S/nw), floor((wi+1)*S/nw)) in 32-bit arithmetic: with S = sq*nw + sr,
-    // floor(wi*S/nw) = wi*sq + floor(wi*sr/nw), and wi*sr < nw^2 fits.
-    const int S = stage_pref[B];
-    const int sq = S / nw, sr = S - sq * nw;
     int lo = wi * sq + (wi * sr) / nw;
     const int hi = (wi + 1) * sq + ((wi + 1) * sr) / nw;
     int b = 0;
@@ -431,9 +435,27 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   // takes a contiguous run of 1 KB chunks and walks it row by row (LDS is read only
   // where the run enters another request).
   {
+    // The waves with a longer stage share (sq + 1 units) take kStageChunks chunks fewer
+    // than the others (none if the tail is short), so they are not the last to finish:
+    // heavy waves split the first C_H chunks equally, the light ones the rest.
     const int C = tail_pref[B];
-    int ci = __builtin_amdgcn_readfirstlane((int)((int64_t)gw * C / nwaves));
-    const int ce = __builtin_amdgcn_readfirstlane((int)((int64_t)(gw + 1) * C / nwaves));
+    const bool heavy = wi < nw && ((wi + 1) * sr) / nw > (wi * sr) / nw;
+    const int heavy_before = G * min((wi * sr) / nw, sr) + (heavy ? group : 0);
+    const int nH = G * sr, nL = nwaves - nH;
+    const int cH = max(0, (int)(((uint32_t)C + (uint32_t)nH * kStageChunks) / (uint32_t)nwaves) - kStageChunks);
+    const int CH = nH * cH, CL = C - CH;
+    int ci, ce;
+    if (heavy) {
+      ci = heavy_before * cH;
+      ce = ci + cH;
+    } else {
+      const int li = gw - heavy_before;  // index among the light waves
+      const int lq = CL / nL, lr = CL - lq * nL;
+      ci = CH + li * lq + (li * lr) / nL;
+      ce = CH + (li + 1) * lq + ((li + 1) * lr) / nL;
+    }
+    ci = __builtin_amdgcn_readfirstlane(ci);
+    ce = __builtin_amdgcn_readfirstlane(ce);
     if (ci < ce) {
       const f32x4 ninf = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
       int b = __builtin_amdgcn_readfirstlane(locate(tail_pref, B, ci));
