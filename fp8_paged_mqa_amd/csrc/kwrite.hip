@@ -9,12 +9,12 @@
 // correctly rounded), code = e4m3fn(x / scale) with x / scale correctly rounded in fp32
 // and then rounded to the nearest code, ties to even; a row of zeros gets scale 1.
 //
-// Mapping: four tokens per wave, one per row of 16 lanes; lane c of a row holds keys
-// [8c, 8c+8) (one 16-byte load of bf16, two of fp32), loaded together with the token's
-// slot. Four DPP row rotations (ror 8, 4, 2, 1) with a NaN-propagating max leave the
+// Mapping: four tokens at a time per wave, one per row of 16 lanes; lane c of a row holds
+// keys [8c, 8c+8) (one 16-byte load of bf16, two of fp32), loaded together with the
+// token's slot, and a wave loads two such groups before converting either. Four DPP row rotations (ror 8, 4, 2, 1) with a NaN-propagating max leave the
 // row's amax in all 16 lanes - no LDS traffic. Each lane stores its 8 codes as one
 // 8-byte store, so a row's 16 lanes write the 128 code bytes contiguously, and lane 0
-// of the row adds the scale. A grid of ceil(T / 16) four-wave workgroups (a stride loop
+// of the row adds the scale. A grid of ceil(T / 32) four-wave workgroups (a stride loop
 // only past 2^20 workgroups). Tokens whose slot lies outside the cache are skipped
 // (negative slots mark padding).
 #include <hip/hip_runtime.h>
@@ -29,6 +29,7 @@ constexpr int kRow = kD + 4;
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
+constexpr int kUnroll = 2;  // groups of 4 tokens per wave and pass (4 and 8 measured no faster)
 
 // Round |y| (finite or not) to the nearest e4m3fn code, ties to even; magnitudes above
 // the tie at 464 (halfway between 448 and 480, which has no code) give NaN, as do NaNs.
@@ -72,26 +73,39 @@ __global__ __launch_bounds__(kThreads) void k_write_kernel(const void* __restric
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane >> 4;  // token of this lane within the wave
   const int c = lane & 15;  // keys [8c, 8c+8)
-  const int64_t first = ((int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave)) * 4;
-  const int64_t stride = (int64_t)gridDim.x * kWaves * 4;
-  for (int64_t base = first; base < T; base += stride) {
-    const int64_t i = base + r < T ? base + r : T - 1;  // rows past T repeat the last (not stored)
-    const int64_t slot = slots[i];                        // issued together with the keys
-    float x[8];
-    if (BF16) {
-      const uint4 v = reinterpret_cast<const uint4*>(k)[i * (kD / 8) + c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const int64_t first = ((int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave)) * 4 * kUnroll;
+  const int64_t stride = (int64_t)gridDim.x * kWaves * 4 * kUnroll;
+  for (int64_t base0 = first; base0 < T; base0 += stride) {
+    // kUnroll groups of 4 tokens: every group's slot and keys are loaded before any is
+    // converted, so a wave has all of its loads in flight at once.
+    int64_t slot_u[kUnroll];
+    float x_u[kUnroll][8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[2 * j] = __uint_as_float(w[j] << 16);
-        x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t bu = base0 + 4 * u;
+      const int64_t i = bu + r < T ? bu + r : T - 1;  // rows past T repeat the last (not stored)
+      slot_u[u] = slots[i];
+      float* x = x_u[u];
+      if (BF16) {
+        const uint4 v = reinterpret_cast<const uint4*>(k)[i * (kD / 8) + c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = __uint_as_float(w[j] << 16);
+          x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        }
+      } else {
+        const float4 v0 = reinterpret_cast<const float4*>(k)[i * (kD / 4) + 2 * c];
+        const float4 v1 = reinterpret_cast<const float4*>(k)[i * (kD / 4) + 2 * c + 1];
+        x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+        x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
       }
-    } else {
-      const float4 v0 = reinterpret_cast<const float4*>(k)[i * (kD / 4) + 2 * c];
-      const float4 v1 = reinterpret_cast<const float4*>(k)[i * (kD / 4) + 2 * c + 1];
-      x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-      x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+    const int64_t base = base0 + 4 * u;
+    const int64_t slot = slot_u[u];
+    const float* x = x_u[u];
     float m = __builtin_fabsf(x[0]);
 #pragma unroll
     for (int j = 1; j < 8; ++j) m = __builtin_elementwise_maximum(m, __builtin_fabsf(x[j]));
@@ -125,13 +139,14 @@ __global__ __launch_bounds__(kThreads) void k_write_kernel(const void* __restric
       // A NaN scale (a NaN key) is written as the canonical quiet NaN.
       if (c == 0) *reinterpret_cast<float*>(row + kD) = __builtin_isnan(scale) ? __builtin_nanf("") : scale;
     }
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_k_write(const KWriteLaunch& a, hipStream_t stream) {
-  const int64_t want = (a.num_tokens + 4 * kWaves - 1) / (4 * kWaves);
+  const int64_t want = (a.num_tokens + 4 * kWaves * kUnroll - 1) / (4 * kWaves * kUnroll);
   const int64_t cap = (int64_t)1 << 20;
   const unsigned blocks = (unsigned)(want < cap ? want : cap);
   if (a.bf16)
