@@ -25,11 +25,11 @@
 //     -inf tail that lie past each request's last stage.
 //     The balance does not depend on how context lengths are distributed, and nothing
 //     is read from the device by the host.
-//   * One wave owns a group of decode rows (at most 4 MFMA row tiles of 16 heads, so at
-//     most 64 query rows for H <= 64). Its query rows stay in VGPRs, already in f16, in
-//     the A-operand layout, for a whole segment. Decode rows beyond one wave's share are
-//     other row groups: other waves walk the same stages for them (their second read of
-//     a key row hits L2).
+//   * One wave owns a group of decode rows (at most 8 MFMA row tiles of 16 heads, 4 with
+//     64-token pages). Its query rows stay in VGPRs, already in f16, in the A-operand
+//     layout, for a whole segment. Decode rows beyond one wave's share are other row
+//     groups: other waves walk the same stages for them (their second read of a key row
+//     hits L2).
 //   * Keys are gathered straight from HBM into the B-operand slots: lane (g, c),
 //     g = lane/16, c = lane%16, owns token c of a 16-token column tile and reads bytes
 //     [16g, 16g+16) and [64+16g, 64+16g+16) of that token's row, so each dwordx4 load
@@ -497,13 +497,14 @@ using KernelFn = void (*)(Params);
 template <int TPJ, int JPG>
 constexpr KernelFn kfn() { return paged_logits_kernel<TPJ, JPG>; }
 
-// [TPJ-1][JPG-1]; TPJ = H/16 in 1..8, JPG = decode rows per wave: min(N, 4/TPJ) for
-// H <= 64 (at most 4 row tiles, 64 f16 query VGPRs), 1 above (up to 8 row tiles).
+// [TPJ-1][JPG-1]; TPJ = H/16 in 1..8, JPG = decode rows per wave: min(N, T/TPJ) with
+// T = 8 row tiles (128 f16 query VGPRs) for pages under 64 tokens and T = 4 (64 VGPRs,
+// two workgroups per CU) otherwise; 1 for H > 64 (up to 8 row tiles).
 constexpr KernelFn kTable[8][4] = {
     {kfn<1, 1>(), kfn<1, 2>(), kfn<1, 3>(), kfn<1, 4>()},
-    {kfn<2, 1>(), kfn<2, 2>(), nullptr, nullptr},
-    {kfn<3, 1>(), nullptr, nullptr, nullptr},
-    {kfn<4, 1>(), nullptr, nullptr, nullptr},
+    {kfn<2, 1>(), kfn<2, 2>(), kfn<2, 3>(), kfn<2, 4>()},
+    {kfn<3, 1>(), kfn<3, 2>(), nullptr, nullptr},
+    {kfn<4, 1>(), kfn<4, 2>(), nullptr, nullptr},
     {kfn<5, 1>(), nullptr, nullptr, nullptr},
     {kfn<6, 1>(), nullptr, nullptr, nullptr},
     {kfn<7, 1>(), nullptr, nullptr, nullptr},
@@ -529,7 +530,12 @@ size_t logits_lds_bytes(int32_t batch) { return (size_t)(3 * (int64_t)batch + 2 
 
 hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   const int tpj = a.heads / 16;
-  const int per_wave = tpj <= 4 ? 4 / tpj : 1;
+  // Decode rows per wave: with pages under 64 tokens a wave holds up to 8 row tiles, so
+  // the key rows of a stage are gathered once for all of a request's decode rows (one
+  // four-wave workgroup per CU leaves each wave the whole register file); with 64-token
+  // pages up to 4, so that two workgroups fit on a CU (measured faster there for N = 4).
+  const int max_tiles = a.block_shift < 6 ? 8 : 4;
+  const int per_wave = tpj <= max_tiles ? max_tiles / tpj : 1;
   const int jpg = a.next_n < per_wave ? a.next_n : per_wave;
   Params p;
   p.q = a.q;
