@@ -16,8 +16,9 @@
 //     v_mfma_f32_16x16x32_f16, four chained per 128-wide row: f16 products of e4m3
 //     values are exact and the fp32 accumulation is correctly rounded.
 //   * Schedule: one round of persistent workgroups (one per CU), so no workgroup waits
-//     for a slot. Each workgroup scans context_lens into LDS prefix sums (DPP wave
-//     scans, one barrier); every
+//     for a slot. Each wave scans context_lens into LDS prefix sums (for up to 64
+//     requests its own copy, one request per lane, no barrier; beyond that one copy per
+//     workgroup, DPP wave scans and one barrier); every
 //     wave then takes an equal contiguous share of the work units of all requests -
 //     each 64-token key stage one unit, and each request's start one more, the cost of
 //     loading another request's table entries and query rows - split at request
@@ -200,22 +201,44 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   constexpr int TILES = TPJ * JPG;  // MFMA row tiles (16 heads each) held by one wave
   static_assert(TILES >= 1 && TILES <= 8, "query tile budget");
 
-  // LDS: clamped ctx per request, key-stage prefix, tail-chunk prefix, scan scratch.
-  extern __shared__ int lds[];
-  const int B = p.B;
-  int* ctx_s = lds;                     // [B]
-  int* stage_pref = lds + B;            // [B+1] work units: stages + kStartUnits each
-  int* tail_pref = stage_pref + B + 1;  // [B+1]
-  int* scan_tmp = tail_pref + B + 1;    // [2 * kWavesPerGroup]
-
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+  // LDS: clamped ctx per request, key-stage prefix, tail-chunk prefix, scan scratch. Up
+  // to 64 requests every wave builds its own copy (one request per lane, no barrier).
+  extern __shared__ int lds[];
+  const int B = p.B;
+  const bool per_wave = B <= kWave;
+  int* ctx_s = lds + (per_wave ? wave * (3 * B + 2) : 0);  // [B]
+  int* stage_pref = ctx_s + B;          // [B+1] work units: stages + kStartUnits each
+  int* tail_pref = stage_pref + B + 1;  // [B+1]
+  int* scan_tmp = tail_pref + B + 1;    // [2 * kWavesPerGroup] (one copy only)
   const int g = lane >> 4;   // lane group: k-slice for operands, row quad for results
   const int c = lane & 15;   // column (token) / row (head) within a 16-wide tile
   const int L = p.L;
 
   // ---- Schedule: per request, the number of 64-token key stages and of tail chunks.
-  {
+  if (per_wave) {
+    int nu = 0, nc = 0;
+    if (lane < B) {
+      const int ctx = max(0, min(p.ctx_lens[lane], min(p.Wt, L)));
+      const int ns = (ctx + kStage - 1) / kStage;
+      const int tail0 = ns * kStage;
+      nc = tail0 < L ? p.N * ((L - tail0 + kTailChunk - 1) / kTailChunk) : 0;
+      nu = ns > 0 ? ns + kStartUnits : 0;
+      ctx_s[lane] = ctx;
+    }
+    const int iu = (int)wave_scan_add((uint32_t)nu), ic = (int)wave_scan_add((uint32_t)nc);
+    if (lane < B) {
+      stage_pref[lane] = iu - nu;
+      tail_pref[lane] = ic - nc;
+    }
+    if (lane == kWave - 1) {  // lanes past B add nothing: the totals
+      stage_pref[B] = iu;
+      tail_pref[B] = ic;
+    }
+    __builtin_amdgcn_wave_barrier();  // the wave reads only what it wrote
+  } else {
     const int per = (B + kThreads - 1) / kThreads;  // requests per thread, consecutive
     const int r0 = threadIdx.x * per;
     int stages = 0, chunks = 0;
@@ -524,7 +547,10 @@ int compute_units() {
   return n;
 }
 
-size_t logits_lds_bytes(int32_t batch) { return (size_t)(3 * (int64_t)batch + 2 + 2 * kWavesPerGroup) * 4; }
+size_t logits_lds_bytes(int32_t batch) {
+  const int64_t copies = batch <= kWave ? kWavesPerGroup : 1;
+  return (size_t)(copies * (3 * (int64_t)batch + 2) + 2 * kWavesPerGroup) * 4;
+}
 
 }  // namespace
 

@@ -108,6 +108,19 @@ def test_other_head_counts(heads, next_n):
     _parity(case, what=f"H={heads} N={next_n}")
 
 
+@pytest.mark.parametrize("batch", [64, 65, 300])
+def test_request_counts(batch):
+    """Up to 64 requests each wave scans the context lengths itself (one per lane); above,
+    the workgroup shares one scan (at 300 requests, two per thread). Empty contexts
+    included."""
+    rng = np.random.default_rng(6000 + batch)
+    ctx = rng.integers(0, 400, batch)
+    ctx[0], ctx[-1], ctx[batch // 2] = 0, 385, 64
+    case = wl.make_case(batch=batch, next_n=2, heads=32, ctx=ctx.tolist(), max_model_len=400,
+                        seed=6000 + batch)
+    _parity(case, what=f"B={batch}")
+
+
 @pytest.mark.parametrize("k", [1, 7, 100, 2047, 2048])
 def test_k_values(k):
     case = wl.make_case(batch=6, next_n=2, heads=32, ctx=[1, 2, 100, 2048, 2050, 9000],
