@@ -448,44 +448,45 @@ __device__ void select_row(const Params& p, int r, int nv, Full& sh) {
   const bool whole = cnt0 == rem;
   // Emit the elements above the threshold bin (the whole bin too when it is all taken)
   // straight to the output row and collect the bin's own elements into the candidate
-  // list. Each wave counts its elements and publishes the counts; after one barrier every
-  // wave takes its first slots from a prefix over the 16 counts and each lane its rank
-  // in the wave's mask. above(bin0) < k, so every output slot is in range; candidate
+  // list. Each lane marks its visible elements in two bit masks (above the bin / in it);
+  // lane and wave prefix sums of the mask populations give every lane its first output
+  // and candidate slots (wave totals through LDS, one barrier), and each lane then walks
+  // only its set bits. above(bin0) < k, so every output slot is in range; candidate
   // slots past kCap are dropped (the finish then refines over the row).
   const uint32_t thr = whole ? bin0 : bin0 + 1;
-  uint32_t na = 0, nb = 0;
+  const int vis = min(PER, (nv - tid + kThreads - 1) / kThreads);  // elements i < vis are visible
+  uint32_t ma = 0, mb = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const uint64_t in = inm(i);
-    na += (uint32_t)__popcll(__ballot(bin[i] >= thr) & in);
-    nb += whole ? 0u : (uint32_t)__popcll(__ballot(bin[i] == bin0) & in);
+    ma |= (bin[i] >= thr ? 1u : 0u) << i;
+    mb |= (bin[i] == bin0 ? 1u : 0u) << i;
   }
-  if (lane == 0) {
-    sh.red[kRedEmit + wave] = na;
-    sh.red[kRedCand + wave] = nb;
+  const uint32_t vmask = vis >= 32 ? ~0u : (1u << max(vis, 0)) - 1u;
+  ma &= vmask;
+  mb = whole ? 0u : (mb & vmask);
+  const uint32_t la = (uint32_t)__popc(ma), lb = (uint32_t)__popc(mb);
+  const uint32_t ia = wave_scan_add(la), ib = wave_scan_add(lb);
+  if (lane == 63) {
+    sh.red[kRedEmit + wave] = ia;
+    sh.red[kRedCand + wave] = ib;
   }
   if (threadIdx.x == 0) sh.n_out = above;  // the finish appends after the emitted elements
   __syncthreads();
   const uint32_t ca = lane < kWaves ? sh.red[kRedEmit + lane] : 0u;
   const uint32_t cb = lane < kWaves ? sh.red[kRedCand + lane] : 0u;
-  uint32_t oa = (uint32_t)__builtin_amdgcn_readlane((int)(row16_prefix(ca) - ca), wave);
-  uint32_t ob = (uint32_t)__builtin_amdgcn_readlane((int)(row16_prefix(cb) - cb), wave);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  uint32_t oa = (uint32_t)__builtin_amdgcn_readlane((int)(row16_prefix(ca) - ca), wave) + ia - la;
+  uint32_t ob = (uint32_t)__builtin_amdgcn_readlane((int)(row16_prefix(cb) - cb), wave) + ib - lb;
+  while (ma) {
+    const int i = __builtin_ctz(ma);
+    ma &= ma - 1u;
+    out[oa++] = i * kThreads + tid;
+  }
+  while (mb) {  // the threshold bin's elements (few): their keys are read again
+    const int i = __builtin_ctz(mb);
+    mb &= mb - 1u;
     const int t = i * kThreads + tid;
-    const uint64_t in = inm(i);
-    const uint64_t ma = __ballot(bin[i] >= thr) & in;
-    const uint32_t ra = __builtin_amdgcn_mbcnt_hi((uint32_t)(ma >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma, oa));
-    if (__builtin_amdgcn_inverse_ballot_w64(ma)) out[ra] = t;
-    oa += (uint32_t)__popcll(ma);
-    if (nb) {  // the threshold bin's elements (few)
-      const uint64_t mb = __ballot(bin[i] == bin0) & in;
-      if (mb) {
-        const uint32_t rb = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, ob));
-        if (__builtin_amdgcn_inverse_ballot_w64(mb) && rb < (uint32_t)kCap) sh.cand[rb] = compose(order_key(v[i]), t);
-        ob += (uint32_t)__popcll(mb);
-      }
-    }
+    if (ob < (uint32_t)kCap) sh.cand[ob] = compose(order_key(row[t]), t);
+    ++ob;
   }
   if (!whole) {
     __syncthreads();  // the candidate list is complete
