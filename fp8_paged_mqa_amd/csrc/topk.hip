@@ -684,23 +684,27 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(Params p) {
     const bool whole = cnt0 == (uint32_t)k - above;
     // Elements above the threshold bin (the whole bin too when all of it is taken) go to
     // the output, the bin's own elements to the row's candidate list; slots from one
-    // pair of global atomics per workgroup, a prefix over the waves' counts and the
-    // lanes' ranks in the ballot masks.
+    // pair of global atomics per workgroup, a prefix over the waves' counts and each
+    // lane's prefix over the populations of its two element masks; each lane then walks
+    // its set bits.
     const uint32_t thr = whole ? bin0 : bin0 + 1;
-    uint64_t ma[kPer], mb[kPer];
-    uint32_t na = 0, nb = 0;
+    const int vis = min(kPer, (cur.nv - cur.base - tid + kThreads - 1) / kThreads);  // visible elements
+    uint32_t ma = 0, mb = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const uint64_t in = __ballot(tid < cur.nv - cur.base - i * kThreads);
       const uint32_t d = order_key(cur.v[i]) >> (32 - kKeyBits);
-      ma[i] = __ballot(d >= thr) & in;
-      mb[i] = whole ? 0ull : (__ballot(d == bin0) & in);
-      na += (uint32_t)__popcll(ma[i]);
-      nb += (uint32_t)__popcll(mb[i]);
+      ma |= (d >= thr ? 1u : 0u) << i;
+      mb |= (d == bin0 ? 1u : 0u) << i;
     }
-    if (lane == 0) {
-      sh.red[kRedEmit + wave] = na;
-      sh.red[kRedCand + wave] = nb;
+    static_assert(kPer < 32, "a lane's element masks fit 32 bits");
+    const uint32_t vmask = (1u << max(vis, 0)) - 1u;
+    ma &= vmask;
+    mb = whole ? 0u : (mb & vmask);
+    const uint32_t la = (uint32_t)__popc(ma), lb = (uint32_t)__popc(mb);
+    const uint32_t la_incl = wave_scan_add(la), lb_incl = wave_scan_add(lb);
+    if (lane == 63) {
+      sh.red[kRedEmit + wave] = la_incl;
+      sh.red[kRedCand + wave] = lb_incl;
     }
     __syncthreads();
     const uint32_t ca = lane < kWaves ? sh.red[kRedEmit + lane] : 0u;
@@ -713,21 +717,22 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(Params p) {
       sh.base_b = tb ? atomicAdd(&p.counters[2 * cur.slot + 1], tb) : 0u;
     }
     __syncthreads();
-    uint32_t oa = sh.base_a + (uint32_t)__builtin_amdgcn_readlane((int)(ia - ca), wave);
-    uint32_t ob = sh.base_b + (uint32_t)__builtin_amdgcn_readlane((int)(ib - cb), wave);
+    uint32_t oa = sh.base_a + (uint32_t)__builtin_amdgcn_readlane((int)(ia - ca), wave) + la_incl - la;
+    uint32_t ob = sh.base_b + (uint32_t)__builtin_amdgcn_readlane((int)(ib - cb), wave) + lb_incl - lb;
     int32_t* out = p.idx + (int64_t)cur.r * k;
     uint64_t* cand = p.cand + (int64_t)cur.slot * kCap;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    while (ma) {
+      const int i = __builtin_ctz(ma);
+      ma &= ma - 1u;
+      const uint32_t ra = oa++;
+      if (ra < (uint32_t)k) out[ra] = cur.base + i * kThreads + tid;
+    }
+    while (mb) {  // the threshold bin's elements (few): their keys are read again
+      const int i = __builtin_ctz(mb);
+      mb &= mb - 1u;
       const int t = cur.base + i * kThreads + tid;
-      const uint32_t ra = __builtin_amdgcn_mbcnt_hi((uint32_t)(ma[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ma[i], oa));
-      if (__builtin_amdgcn_inverse_ballot_w64(ma[i]) && ra < (uint32_t)k) out[ra] = t;
-      oa += (uint32_t)__popcll(ma[i]);
-      if (mb[i]) {  // uniform; the threshold bin's elements (few)
-        const uint32_t rb = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb[i], ob));
-        if (__builtin_amdgcn_inverse_ballot_w64(mb[i]) && rb < (uint32_t)kCap) cand[rb] = compose(order_key(cur.v[i]), t);
-        ob += (uint32_t)__popcll(mb[i]);
-      }
+      const uint32_t rb = ob++;
+      if (rb < (uint32_t)kCap) cand[rb] = compose(order_key(p.logits[(int64_t)cur.r * p.L + t]), t);
     }
     // The next item's first LDS writes (histogram, then the slots above) come after
     // barriers every wave passes only once it has read this item's.
