@@ -16,9 +16,9 @@
 //     v_mfma_f32_16x16x32_f16, four chained per 128-wide row: f16 products of e4m3
 //     values are exact and the fp32 accumulation is correctly rounded.
 //   * Schedule: one round of persistent workgroups (one per CU), so no workgroup waits
-//     for a slot. Each wave scans context_lens into LDS prefix sums (for up to 64
-//     requests its own copy, one request per lane, no barrier; beyond that one copy per
-//     workgroup, DPP wave scans and one barrier); every
+//     for a slot. Each wave scans context_lens into prefix sums (for up to 64 requests
+//     in its own registers, one request per lane, no barrier or LDS; beyond that in LDS,
+//     one copy per workgroup, DPP wave scans and one barrier); every
 //     wave then takes an equal contiguous share of the work units of all requests -
 //     each 64-token key stage one unit, and each request's start one more, the cost of
 //     loading another request's table entries and query rows - split at request
@@ -204,40 +204,38 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
-  // LDS: clamped ctx per request, key-stage prefix, tail-chunk prefix, scan scratch. Up
-  // to 64 requests every wave builds its own copy (one request per lane, no barrier).
+  // More than 64 requests: LDS holds the clamped ctx per request, the work-unit prefix,
+  // the tail-chunk prefix and scan scratch. Up to 64, every wave keeps them in registers
+  // (one request per lane, no barrier) and LDS is not used.
   extern __shared__ int lds[];
   const int B = p.B;
   const bool per_wave = B <= kWave;
-  int* ctx_s = lds + (per_wave ? wave * (3 * B + 2) : 0);  // [B]
+  int* ctx_s = lds;                     // [B]
   int* stage_pref = ctx_s + B;          // [B+1] work units: stages + kStartUnits each
   int* tail_pref = stage_pref + B + 1;  // [B+1]
-  int* scan_tmp = tail_pref + B + 1;    // [2 * kWavesPerGroup] (one copy only)
+  int* scan_tmp = tail_pref + B + 1;    // [2 * kWavesPerGroup]
   const int g = lane >> 4;   // lane group: k-slice for operands, row quad for results
   const int c = lane & 15;   // column (token) / row (head) within a 16-wide tile
   const int L = p.L;
 
   // ---- Schedule: per request, the number of 64-token key stages and of tail chunks.
+  // Up to 64 requests they stay in registers, lane b holding request b (read back with
+  // readlane at a wave-uniform index); beyond, in LDS.
+  int r_ctx = 0, r_pref = 0, r_tail = 0, tot_pref = 0, tot_tail = 0;
   if (per_wave) {
     int nu = 0, nc = 0;
     if (lane < B) {
-      const int ctx = max(0, min(p.ctx_lens[lane], min(p.Wt, L)));
-      const int ns = (ctx + kStage - 1) / kStage;
+      r_ctx = max(0, min(p.ctx_lens[lane], min(p.Wt, L)));
+      const int ns = (r_ctx + kStage - 1) / kStage;
       const int tail0 = ns * kStage;
       nc = tail0 < L ? p.N * ((L - tail0 + kTailChunk - 1) / kTailChunk) : 0;
       nu = ns > 0 ? ns + kStartUnits : 0;
-      ctx_s[lane] = ctx;
     }
     const int iu = (int)wave_scan_add((uint32_t)nu), ic = (int)wave_scan_add((uint32_t)nc);
-    if (lane < B) {
-      stage_pref[lane] = iu - nu;
-      tail_pref[lane] = ic - nc;
-    }
-    if (lane == kWave - 1) {  // lanes past B add nothing: the totals
-      stage_pref[B] = iu;
-      tail_pref[B] = ic;
-    }
-    __builtin_amdgcn_wave_barrier();  // the wave reads only what it wrote
+    r_pref = iu - nu;
+    r_tail = ic - nc;
+    tot_pref = __builtin_amdgcn_readlane(iu, kWave - 1);  // lanes past B add nothing
+    tot_tail = __builtin_amdgcn_readlane(ic, kWave - 1);
   } else {
     const int per = (B + kThreads - 1) / kThreads;  // requests per thread, consecutive
     const int r0 = threadIdx.x * per;
@@ -277,6 +275,16 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
     __syncthreads();
   }
 
+  // Clamped ctx, work-unit prefix and tail-chunk prefix of request i (i <= B for the
+  // prefixes, where entry B is the total); i is wave-uniform.
+  auto ctx_at = [&](int i) { return per_wave ? __builtin_amdgcn_readlane(r_ctx, i) : ctx_s[i]; };
+  auto pref_at = [&](int i) {
+    return per_wave ? (i >= B ? tot_pref : __builtin_amdgcn_readlane(r_pref, i)) : stage_pref[i];
+  };
+  auto tail_at = [&](int i) {
+    return per_wave ? (i >= B ? tot_tail : __builtin_amdgcn_readlane(r_tail, i)) : tail_pref[i];
+  };
+
   const int nwaves = gridDim.x * kWavesPerGroup;
   const int gw = blockIdx.x * kWavesPerGroup + wave;
 
@@ -290,15 +298,15 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   // Share [floor(wi*S/nw), floor((wi+1)*S/nw)) in 32-bit arithmetic: with S = sq*nw + sr,
   // floor(wi*S/nw) = wi*sq + floor(wi*sr/nw), and wi*sr < nw^2 fits. sr waves of each
   // group take sq + 1 units, the others sq.
-  const int S = stage_pref[B];
+  const int S = pref_at(B);
   const int sq = S / nw, sr = S - sq * nw;
   if (wi < nw) {
     int lo = wi * sq + (wi * sr) / nw;
     const int hi = (wi + 1) * sq + ((wi + 1) * sr) / nw;
     int b = 0;
     if (lo < hi) {
-      if (B <= kWave) {  // the prefix entries <= lo are a run from entry 0: count them
-        const uint64_t le = __ballot(lane < B && stage_pref[lane < B ? lane : 0] <= lo);
+      if (per_wave) {  // the prefix entries <= lo are a run from entry 0: count them
+        const uint64_t le = __ballot(lane < B && r_pref <= lo);
         b = __popcll(le) - 1;
       } else {
         b = locate(stage_pref, B, lo);
@@ -309,11 +317,12 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
     while (lo < hi) {
       // Segment: stages [s0, s0 + nstage) of request b, the stages whose units fall in
       // [lo, seg_hi); none when the share holds only the request's start units.
-      const int seg_hi = min(hi, stage_pref[b + 1]);
-      const int s0 = max(lo - stage_pref[b] - kStartUnits, 0);
-      const int nstage = seg_hi - stage_pref[b] - kStartUnits - s0;
+      const int pb = pref_at(b);
+      const int seg_hi = min(hi, pref_at(b + 1));
+      const int s0 = max(lo - pb - kStartUnits, 0);
+      const int nstage = seg_hi - pb - kStartUnits - s0;
       if (nstage > 0) {
-        const int ctx = ctx_s[b];
+        const int ctx = ctx_at(b);
         const int t0 = s0 * kStage;
         const int t_end = min((s0 + nstage) * kStage, L);
         const int t_need = min(t_end, ctx);
@@ -450,7 +459,7 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
 
       lo = seg_hi;
       ++b;
-      while (b < B && stage_pref[b + 1] <= lo) ++b;  // skip requests without stages
+      while (b < B && pref_at(b + 1) <= lo) ++b;  // skip requests without stages
     }
   }
 
@@ -461,7 +470,7 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
     // The waves with a longer stage share (sq + 1 units) take kStageChunks chunks fewer
     // than the others (none if the tail is short), so they are not the last to finish:
     // heavy waves split the first C_H chunks equally, the light ones the rest.
-    const int C = tail_pref[B];
+    const int C = tail_at(B);
     const bool heavy = wi < nw && ((wi + 1) * sr) / nw > (wi * sr) / nw;
     const int heavy_before = G * min((wi * sr) / nw, sr) + (heavy ? group : 0);
     const int nH = G * sr, nL = nwaves - nH;
@@ -481,15 +490,16 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
     ce = __builtin_amdgcn_readfirstlane(ce);
     if (ci < ce) {
       const f32x4 ninf = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-      int b = __builtin_amdgcn_readfirstlane(locate(tail_pref, B, ci));
+      int b = per_wave ? __popcll(__ballot(lane < B && r_tail <= ci)) - 1 : locate(tail_pref, B, ci);
+      b = __builtin_amdgcn_readfirstlane(b);
       int tail0 = 0, per_row = 1, j = 0, k = 0;
       auto enter = [&](int local) {  // request b, chunk `local` of its N rows
-        tail0 = __builtin_amdgcn_readfirstlane(((ctx_s[b] + kStage - 1) / kStage) * kStage);
+        tail0 = __builtin_amdgcn_readfirstlane(((ctx_at(b) + kStage - 1) / kStage) * kStage);
         per_row = (L - tail0 + kTailChunk - 1) / kTailChunk;
         j = local / per_row;
         k = local - j * per_row;
       };
-      enter(ci - __builtin_amdgcn_readfirstlane(tail_pref[b]));
+      enter(ci - __builtin_amdgcn_readfirstlane(tail_at(b)));
       for (;;) {
         float* rp = p.out + (int64_t)(b * p.N + j) * L;
         const int start = tail0 + k * kTailChunk;
@@ -506,8 +516,8 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         if (++k == per_row) {
           k = 0;
           if (++j == p.N) {  // the next request that has a tail
-            while (b + 1 < B && __builtin_amdgcn_readfirstlane(tail_pref[b + 1]) <= ci) ++b;
-            enter(ci - __builtin_amdgcn_readfirstlane(tail_pref[b]));
+            while (b + 1 < B && __builtin_amdgcn_readfirstlane(tail_at(b + 1)) <= ci) ++b;
+            enter(ci - __builtin_amdgcn_readfirstlane(tail_at(b)));
           }
         }
       }
@@ -547,9 +557,9 @@ int compute_units() {
   return n;
 }
 
+// Up to 64 requests the schedule lives in registers and the kernel uses no LDS.
 size_t logits_lds_bytes(int32_t batch) {
-  const int64_t copies = batch <= kWave ? kWavesPerGroup : 1;
-  return (size_t)(copies * (3 * (int64_t)batch + 2) + 2 * kWavesPerGroup) * 4;
+  return batch <= kWave ? 0 : (size_t)(3 * (int64_t)batch + 2 + 2 * kWavesPerGroup) * 4;
 }
 
 }  // namespace
