@@ -393,17 +393,17 @@ __device__ void select_row(const Params& p, int r, int nv, Full& sh) {
   }
   for (int i = threadIdx.x; i < kKeyBins; i += kThreads) sh.hist[i] = 0;
   // Min / max of the visible values; a non-finite value anywhere switches to key bins
-  // (the wave reports it as an infinite maximum).
+  // (the wave reports it as an infinite maximum). The maximum propagates NaN, so one test
+  // of the lane's extremes finds any NaN or infinity among its values.
   float lo = __builtin_inff(), hi = -__builtin_inff();
-  uint64_t bad = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     lo = fminf(lo, v[i]);
-    hi = fmaxf(hi, v[i]);
-    bad |= __ballot(!__builtin_isfinite(v[i]));
+    hi = __builtin_elementwise_maximum(hi, v[i]);
   }
+  const uint64_t bad = __ballot(!__builtin_isfinite(hi) || !__builtin_isfinite(lo));
   lo = wave_scan_minmax<false>(lo);
-  hi = wave_scan_minmax<true>(hi);
+  hi = wave_scan_minmax<true>(bad ? -__builtin_inff() : hi);
   if (lane == 63) {
     sh.red[kRedLo + wave] = __float_as_uint(lo);
     sh.red[kRedHi + wave] = __float_as_uint(bad ? __builtin_inff() : hi);
