@@ -102,7 +102,7 @@ def test_named_workload(name):
 
 
 @pytest.mark.parametrize("heads,next_n", [(16, 1), (48, 3), (80, 1), (96, 2), (112, 1), (128, 4),
-                                           (32, 3), (64, 3)])
+                                           (32, 3), (64, 3), (80, 3), (128, 3)])
 def test_other_head_counts(heads, next_n):
     case = wl.make_case(batch=5, next_n=next_n, heads=heads, ctx=[1, 70, 2049, 300, 4100],
                         max_model_len=4200, seed=3000 + heads + next_n)
