@@ -19,24 +19,25 @@
 //            so bins are ordered like the logits; rows holding a non-finite value use the
 //            top 12 key bits instead, constant rows a single bin). An LDS histogram and a
 //            scan from the top find the bin holding the k-th element (every wave finishes
-//            the search itself after one barrier). Each wave counts its elements above
-//            that bin and in it and publishes the counts; after one barrier it takes its
-//            first slots from a prefix over the 16 counts and each lane its rank in the
-//            wave's ballot mask: positions above the bin go straight to the output row,
-//            the bin's own elements to an LDS candidate list. A small list is finished by
+//            the search itself after one barrier). Each lane marks its elements above
+//            that bin and in it in two bit masks; a lane scan of the mask populations and
+//            the 16 wave totals (one barrier) give every lane its first slots, and each
+//            lane walks its set bits: positions above the bin go straight to the output
+//            row, the bin's own elements to an LDS candidate list. A small list is finished by
 //            counting, for each candidate, the candidates above it (the count is the
 //            slot); a large one by further 11-bit radix digits of e, or over the whole
 //            row if the bin holds more than the list (kCap). One CU serves a row, so the
 //            time is set by the instructions each wave issues: per-element work is kept
 //            to a few vector instructions (buffer loads clamped onto the last visible
-//            element, lane masks from one compare each, emission by mask rank).
+//            element, lane masks from one compare each, a NaN-propagating maximum for the
+//            finiteness test, emission by walking set bits).
 //   long     nv > 8192 when max_model_len > 32768: 8192-element chunks. A
 //            schedule kernel lists the rows of each class and the long rows' chunks and
 //            clears their histograms; persistent kernels then add each chunk's 12-bit key
 //            histogram into the row's global histogram (the next chunk's loads in flight
 //            meanwhile), emit each chunk's elements above the threshold bin (slots from
 //            one pair of global atomics per workgroup, a prefix over the waves' counts
-//            and the lanes' ballot ranks) and collect its threshold-bin elements, and
+//            and the lanes' mask populations) and collect its threshold-bin elements, and
 //            finish each row's candidates in LDS. If the threshold bin holds more than
 //            kCap elements (extreme ties, e.g. a constant row) the finish refines over
 //            the whole row from global memory: slower, same result. The finishing pass's
