@@ -194,8 +194,8 @@ __device__ __forceinline__ int locate(const int* a, int n, int x) {
   return lo;
 }
 
-// Up to 4 row tiles fit two waves per SIMD (<= 256 VGPRs); the 5..8-tile variants
-// (H > 64) take the whole register file.
+// Up to 4 row tiles fit two waves per SIMD (<= 256 VGPRs); the 5..8-tile variants (H > 64,
+// or several decode rows per wave with pages under 64 tokens) take the whole register file.
 template <int TPJ, int JPG>
 __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logits_kernel(Params p) {
   constexpr int TILES = TPJ * JPG;  // MFMA row tiles (16 heads each) held by one wave
