@@ -73,3 +73,32 @@ def test_k_write_blocked_cache_and_logits():
                           case.max_model_len, case.next_n)
     g, _ = run_gpu(written)
     check_logits(g, oracle_logits(written), "logits of written cache")
+
+
+def test_k_write_benchmark_size():
+    """The call `bench.py --op kwrite` times: 65 536 bf16 tokens (normal keys times a
+    lognormal magnitude per token) into permuted slots of a 600 000-row cache, in one
+    launch. Every written row is compared with the oracle's quantisation of its token, and
+    every other row must still be zero."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    T, nslots = 65536, 600_000
+    k32 = (rng.standard_normal((T, 128), dtype=np.float32)
+           * rng.lognormal(0, 1, size=(T, 1)).astype(np.float32))
+    k = torch.from_numpy(k32).to(torch.bfloat16)
+    slots = rng.permutation(nslots)[:T].astype(np.int64)
+    say(f"[gpu] k write benchmark size T={T} slots={nslots}")
+    kv = torch.zeros((nslots, 132), dtype=torch.uint8, device="cuda")
+    mqa.mqa_indexer_k_write(k.cuda(), torch.from_numpy(slots).cuda(), kv)
+    torch.cuda.synchronize()
+    got = kv.cpu().numpy()
+    keys = k.float().numpy()
+    want = np.zeros((T, 132), np.uint8)
+    for i in range(T):
+        codes, scale = oracle.quantize_k_row(keys[i])
+        want[i, :128] = codes
+        want[i, 128:] = np.frombuffer(np.float32(scale).astype("<f4").tobytes(), dtype=np.uint8)
+    diff = np.flatnonzero((got[slots] != want).any(axis=1))
+    assert diff.size == 0, f"{diff.size} of {T} rows differ, first tokens {diff[:5]}"
+    untouched = np.ones(nslots, bool)
+    untouched[slots] = False
+    assert not got[untouched].any(), "a row outside the slot mapping was written"
