@@ -252,3 +252,14 @@ def test_sparse_mla_workspace():
     assert call_mla(big, ws=FAKE, ws_bytes=need - 1) == mqa.MQA_ERR_WORKSPACE
     assert mqa.mqa_sparse_mla_workspace_bytes(mla_shape(batch=1, next_n=1, topk=64)) == 0
     assert mqa.mqa_sparse_mla_workspace_bytes(mla_shape(heads=8)) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it says so and exits non-zero before it
+    touches a device (runs here, without a GPU)."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
