@@ -71,7 +71,7 @@ const char* mqa_status_string(int status) {
              "block_table_stride * block_size and, for block_size > 1, num_blocks * block_size "
              "below 2^31), heads a multiple of 16 up to 128, "
              "next_n 1..4, max_model_len <= 2^30, batch <= 8192 and batch * next_n * (ceil(max_model_len / 64) + 1) < 2^31 for the logits, k 1..2048, non-paged n <= 2^29, 16-byte aligned q and weights, "
-             "4-byte aligned kv_cache, logits, idx and integer arrays; sparse MLA decode: heads 16, "
+             "4-byte aligned kv_cache, logits, idx and integer arrays, 16-byte aligned top-k workspace; sparse MLA decode: heads 16, "
              "head_dim 576, v_dim 512, rows <= 65535, topk <= 2^20, 16-byte aligned q, kv_cache, out and workspace";
     case MQA_ERR_WORKSPACE: return "workspace missing or too small";
     case MQA_ERR_HIP: return "HIP launch error";
@@ -125,7 +125,7 @@ int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model
   if (k < 1) return MQA_ERR_SHAPE;
   if (k > kMaxTopk) return MQA_ERR_UNSUPPORTED;
   const size_t need = mqa_topk_workspace_bytes(shape, max_model_len, k);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 8)))
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
     return MQA_ERR_WORKSPACE;
   if (shape->batch == 0) return MQA_OK;
   if (!logits || !context_lens || !idx) return MQA_ERR_NULL;

@@ -25,7 +25,7 @@ struct TopkLaunch {
   const float* logits;
   const int32_t* ctx_lens;
   int32_t* idx;
-  void* workspace;  // topk_workspace_bytes(rows, max_model_len) bytes, 8-byte aligned
+  void* workspace;  // topk_workspace_bytes(rows, max_model_len) bytes, 16-byte aligned
   int32_t batch, next_n, max_model_len, k;
   int32_t token_capacity;  // block_table_stride * block_size: tokens a table row can address
 };

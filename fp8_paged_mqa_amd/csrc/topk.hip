@@ -792,23 +792,24 @@ __global__ __launch_bounds__(kThreads) void topk_finish_kernel(Params p) {
 }
 
 // Workspace layout (long-row mode): meta[8] | long_rows | short_rows | triv_rows |
-// chunk_items | counters | hist | cand, each region 8-byte aligned.
+// chunk_items | counters | hist | cand, each region 16-byte aligned (the histograms are
+// read as uint4; the workspace base is 16-byte aligned).
 struct Layout {
   size_t meta, long_rows, short_rows, triv_rows, chunk_items, counters, hist, cand, total;
 };
 
 Layout layout(int64_t rows, int32_t L) {
-  auto up8 = [](size_t x) { return (x + 7) & ~(size_t)7; };
+  auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
   const int64_t nchunk = (L + kChunk - 1) / kChunk;
   Layout l;
   l.meta = 0;
   l.long_rows = 32;
-  l.short_rows = up8(l.long_rows + 4 * rows);
-  l.triv_rows = up8(l.short_rows + 4 * rows);
-  l.chunk_items = up8(l.triv_rows + 4 * rows);
-  l.counters = up8(l.chunk_items + 8 * rows * nchunk);
-  l.hist = up8(l.counters + 8 * rows);
-  l.cand = up8(l.hist + (size_t)4 * kKeyBins * rows);
+  l.short_rows = up16(l.long_rows + 4 * rows);
+  l.triv_rows = up16(l.short_rows + 4 * rows);
+  l.chunk_items = up16(l.triv_rows + 4 * rows);
+  l.counters = up16(l.chunk_items + 8 * rows * nchunk);
+  l.hist = up16(l.counters + 8 * rows);
+  l.cand = up16(l.hist + (size_t)4 * kKeyBins * rows);
   l.total = l.cand + (size_t)8 * kCap * rows;
   return l;
 }

@@ -87,18 +87,20 @@ typedef struct mqa_shape {
  *     out[r*max_model_len + t] = sum_h weights[r*H + h] * relu(scale * (q[b,j,h,:] . k))
  * Every other slot of the row, t in [visible, max_model_len), is written with -inf.
  *
- *   q               uint8  [B, N, H, 128]   e4m3fn, contiguous
+ *   q               uint8  [B, N, H, 128]   e4m3fn, contiguous, 16-byte aligned
  *   kv_cache        uint8  [num_blocks, S, 132] per token: 128 e4m3fn key bytes, then
  *                                            the fp32 scale; rows are 4-byte aligned
  *                                            (the pointer must be too)
- *   weights         float  [B*N, H]
- *   context_lens    int32  [B]
- *   block_tables    int32  [B, W]
+ *   weights         float  [B*N, H]         16-byte aligned
+ *   context_lens    int32  [B]              4-byte aligned
+ *   block_tables    int32  [B, W]           4-byte aligned
  *   max_model_len   L >= 1, the length of each output row; B * N * (ceil(L/64) + 1)
  *                   must stay below 2^31 (the work is counted in 32-bit units), else
  *                   MQA_ERR_UNSUPPORTED
- *   out             float  [B*N, L]         every element is written
+ *   out             float  [B*N, L]         every element is written; 4-byte aligned (rows
+ *                                            that are 16-byte aligned are written faster)
  *   shape, stream   see above
+ * A pointer with less than the alignment stated is rejected with MQA_ERR_UNSUPPORTED.
  * Accuracy: fp8 x fp8 products are exact, accumulated in fp32; relu, weight and head
  * sum in fp32. Results agree with the exact definition to 5e-3 + 1e-3*|logit| on the
  * supported distributions; NaN key codes or NaN/Inf scales propagate as NaN.
@@ -121,13 +123,15 @@ int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* wei
  * NaN logits are ordered by their bit patterns (positive NaN above +inf).
  *
  *   logits          float  [B*N, L]   as written by mqa_paged_logits (only the visible
- *                                     prefix of each row is read)
- *   context_lens    int32  [B]
- *   max_model_len   L, the row stride of logits
+ *                                     prefix of each row is read), 4-byte aligned
+ *   context_lens    int32  [B]        4-byte aligned
+ *   max_model_len   L, the row stride of logits. Not among the two arguments the
+ *                   operation itself needs (logits and context lengths): it is the
+ *                   row stride, and it bounds the visible prefix like the logits call
  *   k               1 .. 2048
- *   idx             int32  [B*N, k]
+ *   idx             int32  [B*N, k]   4-byte aligned
  *   workspace       device scratch of at least mqa_topk_workspace_bytes(shape,
- *                   max_model_len, k) bytes, 8-byte aligned (may be NULL when that
+ *                   max_model_len, k) bytes, 16-byte aligned (may be NULL when that
  *                   size is 0, i.e. max_model_len <= 32768); contents on entry do not
  *                   matter, the call initialises what it uses, in stream order. Calls
  *                   that overlap in time must not share a workspace.

@@ -110,7 +110,10 @@ def sparse_mla_decode(q, q_scale, kv_cache, kv_scale, indices, block_tables, nex
 
 def sparse_mla_error_bound(q, q_scale, kv_cache, kv_scale, indices, block_tables, next_n, sm_scale):
     """Per output element, kv_scale * sum_t p(h, t) * |k_t[c]| (float64, [R, H, 512]):
-    the magnitude a relative error in the probabilities is measured against."""
+    the magnitude a relative error in the probabilities is measured against. By the
+    triangle inequality it bounds |out| and equals it where the listed values of a column
+    share one sign; with one listed position it is kv_scale * |k_t|, with a zero query
+    kv_scale times the mean of |k_t| over the list."""
     qb = np.asarray(q, dtype=np.uint8)
     qb = qb.reshape(-1, qb.shape[-2], qb.shape[-1])
     R, H, _ = qb.shape

@@ -181,6 +181,80 @@ def pin_mla_block_size_identity(mla):
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
 
 
+def _bound(mla, case):
+    return mla.sparse_mla_error_bound(case.q, case.q_scale, case.kv_cache, case.kv_scale, case.indices,
+                                      case.block_tables, case.next_n, case.sm_scale)
+
+
+def pin_mla_bound_closed_forms(mla):
+    """The tolerance scale B[r, h, c] = kv_scale * sum_t p(h, t) * |v_t[c]| in closed forms:
+    one listed position gives kv_scale * |v_t|; a zero query gives kv_scale times the mean
+    of |v_t| over the list (a duplicate counted twice); positions [a, b, a] give
+    kv_scale * (2x|v_a| + y|v_b|) / (2x + y) with x = e^(s_a - m), y = e^(s_b - m) from
+    plain Python loops; a saturated softmax gives kv_scale * |v_top|. Values decoded by
+    torch, absolute values taken here."""
+    # one position per row
+    case = wl.make_mla_case(batch=2, next_n=1, ctx=[50, 9], topk=8, seed=31)
+    case.indices[:, 1:] = -1
+    bnd = _bound(mla, case)
+    for r in range(2):
+        v = _torch_decode(_row_of(case, r, int(case.indices[r, 0])))[:DV]
+        assert np.array_equal(bnd[r], np.broadcast_to(case.kv_scale * np.abs(v), (H, DV))), r
+    # zero query: uniform weights over the listed entries
+    case = wl.make_mla_case(batch=2, next_n=2, ctx=[30, 12], topk=10, seed=32)
+    case.q[:] = 0
+    case.indices[3, 4] = case.indices[3, 1]
+    bnd = _bound(mla, case)
+    for r in range(case.rows):
+        pos = [int(t) for t in case.indices[r] if t >= 0]
+        mags = [np.abs(_torch_decode(_row_of(case, r // 2, t))[:DV]) for t in pos]
+        want = case.kv_scale * sum(mags) / len(pos)
+        assert _close(bnd[r], np.broadcast_to(want, (H, DV)), rel=1e-13), r
+    # [a, b, a] with plain exponentials
+    case = wl.make_mla_case(batch=1, next_n=1, ctx=[40], topk=3, seed=33)
+    a, bb = int(case.indices[0, 0]), int(case.indices[0, 1])
+    case.indices[0] = [a, bb, a]
+    bnd = _bound(mla, case)
+    ka, kb = _torch_decode(_row_of(case, 0, a)), _torch_decode(_row_of(case, 0, bb))
+    qv = _torch_decode(case.q[0])
+    c = case.sm_scale * case.q_scale * case.kv_scale
+    for h in range(H):
+        sa = sum(float(qv[h, i]) * float(ka[i]) for i in range(D)) * c
+        sb = sum(float(qv[h, i]) * float(kb[i]) for i in range(D)) * c
+        mx = max(sa, sb)
+        x, y = math.exp(sa - mx), math.exp(sb - mx)
+        want = [case.kv_scale * (2 * x * abs(float(ka[i])) + y * abs(float(kb[i]))) / (2 * x + y) for i in range(DV)]
+        assert _close(bnd[0, h], np.array(want), rel=1e-11), h
+    # saturated softmax: scores ~1e7 apart
+    case = wl.make_mla_case(batch=1, next_n=1, ctx=[6], topk=6, table="identity", seed=34)
+    case.q[:] = 0x7E
+    rows = case.kv_cache.reshape(-1, D)
+    order = [int(t) for t in case.indices[0]]
+    for i, t in enumerate(order):
+        rows[t] = 0x00
+        rows[t, :DV] = 0x30 + i
+    rows[order[-1]] = 0x7E
+    rows[order[-1], 1:DV:2] = 0xFE                    # -448 in the odd value dims
+    bnd = _bound(mla, case)
+    assert np.array_equal(bnd[0], np.full((H, DV), case.kv_scale * 448.0))
+
+
+def pin_mla_bound_dominates_output(mla):
+    """Triangle inequality: |out| <= B in every element, with equality (to rounding) in
+    the value columns whose listed entries all share one sign; B is the bound of the
+    rows the row's own request lists (rows of request b read table row b)."""
+    case = wl.make_mla_case(batch=3, next_n=2, ctx=[60, 33, 90], topk=4, block_size=4, seed=35)
+    out, _ = _run(mla, case)
+    bnd = _bound(mla, case)
+    assert np.all(np.abs(out) <= bnd * (1 + 1e-12) + 1e-300)
+    for r in range(case.rows):
+        pos = [int(t) for t in case.indices[r] if t >= 0]
+        vals = np.stack([_torch_decode(_row_of(case, r // 2, t))[:DV] for t in pos])
+        same = np.all(vals >= 0, axis=0) | np.all(vals <= 0, axis=0)
+        assert same.any(), r
+        assert np.allclose(np.abs(out[r][:, same]), bnd[r][:, same], rtol=1e-12, atol=0), r
+
+
 MLA_PINS = [
     pin_mla_matches_torch_sdpa,
     pin_mla_single_position,
@@ -189,4 +263,6 @@ MLA_PINS = [
     pin_mla_saturated_softmax,
     pin_mla_padding_order_and_empty,
     pin_mla_block_size_identity,
+    pin_mla_bound_closed_forms,
+    pin_mla_bound_dominates_output,
 ]

@@ -130,6 +130,18 @@ def test_empty_batch_is_a_no_op():
     assert call_topk(good_shape(batch=0), ptrs=(None,) * 3) == mqa.MQA_OK
 
 
+def test_topk_workspace_alignment_and_size():
+    # rows longer than 32768 need the workspace: missing, short or not 16-byte aligned
+    # are all MQA_ERR_WORKSPACE, checked before any pointer is used
+    shape = good_shape(block_table_stride=40000)
+    need = mqa.mqa_topk_workspace_bytes(shape, 40000, 2048)
+    assert need > 0
+    assert call_topk(shape, L=40000) == mqa.MQA_ERR_WORKSPACE
+    assert call_topk(shape, L=40000, ws=ctypes.c_void_p(0x10000), ws_bytes=need - 1) == mqa.MQA_ERR_WORKSPACE
+    assert call_topk(shape, L=40000, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == mqa.MQA_ERR_WORKSPACE
+    assert mqa.mqa_topk_workspace_bytes(shape, 32768, 2048) == 0
+
+
 def test_workspace_size_query():
     assert mqa.mqa_topk_workspace_bytes(good_shape(), 100, 2048) >= 0
     assert mqa.mqa_topk_workspace_bytes(good_shape(block_size=3), 100, 2048) == 0

@@ -109,15 +109,16 @@ def test_other_head_counts(heads, next_n):
     _parity(case, what=f"H={heads} N={next_n}")
 
 
-@pytest.mark.parametrize("batch", [64, 65, 300])
-def test_request_counts(batch):
+@pytest.mark.parametrize("batch,max_ctx", [(64, 400), (65, 400), (300, 400), (5500, 40), (8192, 24)])
+def test_request_counts(batch, max_ctx):
     """Up to 64 requests each wave scans the context lengths itself (one per lane); above,
-    the workgroup shares one scan (at 300 requests, two per thread). Empty contexts
-    included."""
+    the workgroup shares one scan in LDS (at 300 requests two per thread; at 5500 and at
+    the largest batch the call accepts, 8192, 22 and 32 per thread and more than 64 KB of
+    LDS). Empty contexts included."""
     rng = np.random.default_rng(6000 + batch)
-    ctx = rng.integers(0, 400, batch)
-    ctx[0], ctx[-1], ctx[batch // 2] = 0, 385, 64
-    case = wl.make_case(batch=batch, next_n=2, heads=32, ctx=ctx.tolist(), max_model_len=400,
+    ctx = rng.integers(0, max_ctx, batch)
+    ctx[0], ctx[-1], ctx[batch // 2] = 0, max_ctx - 15, min(64, max_ctx - 1)
+    case = wl.make_case(batch=batch, next_n=2, heads=32, ctx=ctx.tolist(), max_model_len=max_ctx,
                         seed=6000 + batch)
     _parity(case, what=f"B={batch}")
 

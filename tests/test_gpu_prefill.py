@@ -59,13 +59,19 @@ def test_prefill_arbitrary_windows_and_stride():
 
 def test_prefill_large_sampled():
     """The shape the page's prefill reproducer reaches (M = 4096, N = 8192, 32 heads),
-    causal; the oracle checks 24 rows spread over M, element by element."""
+    causal. Every one of the 4096 rows must hold finite values exactly inside its window
+    [0, N - M + m + 1) and -inf everywhere else (the windows need no oracle); 24 rows
+    spread over M are compared with the oracle element by element."""
     M, N, H = 4096, 8192, 32
     q, k, sc, w = _inputs(M, N, H, seed=92)
     ks = np.zeros(M, int)
     ke = np.arange(M) + (N - M) + 1
     say(f"[gpu] prefill M={M} N={N} H={H}")
     g = _run(q, k, sc, w, ks, ke)
+    col = np.arange(N)[None, :]
+    inside = (col >= ks[:, None]) & (col < ke[:, None])
+    assert np.array_equal(np.isneginf(g), ~inside), "-inf pattern of the full output"
+    assert np.all(np.isfinite(g[inside])), "a slot inside a window is not finite"
     rows = np.unique(np.r_[0, 1, 15, 16, 17, 255, 1000, 2047, 2048, 4095, np.random.default_rng(93).integers(0, M, 14)])
     o = oracle.mqa_logits(q[rows], k, sc, w[rows], ks[rows], ke[rows])
     check_logits(g[rows], o, "prefill large (sampled rows)")

@@ -106,6 +106,20 @@ MLA_MUTANTS = [
     ("block slot ignored", "return entries * block_size + t % block_size", "return entries * block_size"),
     ("request of a row taken modulo", "b = r // next_n\n        pos", "b = r % next_n\n        pos"),
     ("query of row 0 for every row", "score = (keys @ qv[r].T) * c", "score = (keys @ qv[0].T) * c"),
+    # the tolerance scale of the GPU tests, B = kv_scale * sum_t p |v_t|
+    ("bound: kv_scale dropped", "bound[r] = float(np.float32(kv_scale)) * (p.T @ np.abs(keys[:, :MLA_V_DIM]))",
+     "bound[r] = p.T @ np.abs(keys[:, :MLA_V_DIM])"),
+    ("bound: absolute value dropped", "bound[r] = float(np.float32(kv_scale)) * (p.T @ np.abs(keys[:, :MLA_V_DIM]))",
+     "bound[r] = float(np.float32(kv_scale)) * (p.T @ keys[:, :MLA_V_DIM])"),
+    ("bound: probabilities unnormalised", "e = np.exp(score - score.max(axis=0))\n        p = e / e.sum(axis=0)",
+     "e = np.exp(score - score.max(axis=0))\n        p = e"),
+    ("bound: maximum not subtracted", "e = np.exp(score - score.max(axis=0))\n        p = e / e.sum(axis=0)",
+     "e = np.exp(score)\n        p = e / e.sum(axis=0)"),
+    ("bound: softmax scale dropped", "c = float(np.float32(sm_scale)) * float(np.float32(q_scale)) * float(np.float32(kv_scale))\n    bound",
+     "c = float(np.float32(q_scale)) * float(np.float32(kv_scale))\n    bound"),
+    ("bound: values from the wrong dims", "(p.T @ np.abs(keys[:, :MLA_V_DIM]))", "(p.T @ np.abs(keys[:, 64:]))"),
+    ("bound: request of a row taken modulo", "tables[r // next_n], S)", "tables[r % next_n], S)"),
+    ("bound: scaled by 10", "bound[r] = float(np.float32(kv_scale)) *", "bound[r] = 10.0 * float(np.float32(kv_scale)) *"),
 ]
 
 
