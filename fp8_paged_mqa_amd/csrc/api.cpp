@@ -57,6 +57,36 @@ int check_mla_shape(const mqa_mla_shape* s) {
   return MQA_OK;
 }
 
+// Checks shared by both top-k entry points that do not involve the workspace.
+int check_topk(const mqa_shape* shape, int32_t max_model_len, int32_t k) {
+  const int st = check_shape(shape, max_model_len);
+  if (st != MQA_OK) return st;
+  if (k < 1) return MQA_ERR_SHAPE;
+  if (k > kMaxTopk) return MQA_ERR_UNSUPPORTED;
+  return MQA_OK;
+}
+
+int check_topk_data(const float* logits, const int32_t* context_lens, const int32_t* idx) {
+  if (!logits || !context_lens || !idx) return MQA_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(context_lens, 4) || !aligned(idx, 4)) return MQA_ERR_UNSUPPORTED;
+  return MQA_OK;
+}
+
+int launch_topk_checked(const float* logits, const int32_t* context_lens, int32_t max_model_len, int32_t k,
+                        int32_t* idx, const mqa_shape* shape, void* workspace, hipStream_t stream) {
+  mqa::TopkLaunch a;
+  a.logits = logits;
+  a.ctx_lens = context_lens;
+  a.idx = idx;
+  a.workspace = workspace;
+  a.batch = shape->batch;
+  a.next_n = shape->next_n;
+  a.token_capacity = shape->block_table_stride * shape->block_size;
+  a.max_model_len = max_model_len;
+  a.k = k;
+  return mqa::launch_topk(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -75,6 +105,8 @@ const char* mqa_status_string(int status) {
              "head_dim 576, v_dim 512, rows <= 65535, topk <= 2^20, 16-byte aligned q, kv_cache, out and workspace";
     case MQA_ERR_WORKSPACE: return "workspace missing or too small";
     case MQA_ERR_HIP: return "HIP launch error";
+    case MQA_ERR_SCRATCH:
+      return "the problem needs more device scratch than the library's static buffer holds (64 MiB per device)";
     default: return "unknown status";
   }
 }
@@ -117,30 +149,31 @@ size_t mqa_topk_workspace_bytes(const mqa_shape* shape, int32_t max_model_len, i
   return mqa::topk_workspace_bytes((int64_t)shape->batch * shape->next_n, max_model_len);
 }
 
+
 int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model_len, int32_t k,
              int32_t* idx, const mqa_shape* shape, void* workspace, size_t workspace_bytes,
              hipStream_t stream) {
-  const int st = check_shape(shape, max_model_len);
+  int st = check_topk(shape, max_model_len, k);
   if (st != MQA_OK) return st;
-  if (k < 1) return MQA_ERR_SHAPE;
-  if (k > kMaxTopk) return MQA_ERR_UNSUPPORTED;
   const size_t need = mqa_topk_workspace_bytes(shape, max_model_len, k);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
     return MQA_ERR_WORKSPACE;
   if (shape->batch == 0) return MQA_OK;
-  if (!logits || !context_lens || !idx) return MQA_ERR_NULL;
-  if (!aligned(logits, 4) || !aligned(context_lens, 4) || !aligned(idx, 4)) return MQA_ERR_UNSUPPORTED;
-  mqa::TopkLaunch a;
-  a.logits = logits;
-  a.ctx_lens = context_lens;
-  a.idx = idx;
-  a.workspace = workspace;
-  a.batch = shape->batch;
-  a.next_n = shape->next_n;
-  a.token_capacity = shape->block_table_stride * shape->block_size;
-  a.max_model_len = max_model_len;
-  a.k = k;
-  return mqa::launch_topk(a, stream) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+  if ((st = check_topk_data(logits, context_lens, idx)) != MQA_OK) return st;
+  return launch_topk_checked(logits, context_lens, max_model_len, k, idx, shape, workspace, stream);
+}
+
+int mqa_topk_noalloc(const float* logits, const int32_t* context_lens, int32_t max_model_len, int32_t k,
+                     int32_t* idx, const mqa_shape* shape, hipStream_t stream) {
+  int st = check_topk(shape, max_model_len, k);
+  if (st != MQA_OK) return st;
+  const size_t need = mqa_topk_workspace_bytes(shape, max_model_len, k);
+  if (need > mqa::topk_static_scratch_bytes()) return MQA_ERR_SCRATCH;
+  if (shape->batch == 0) return MQA_OK;
+  if ((st = check_topk_data(logits, context_lens, idx)) != MQA_OK) return st;
+  void* ws = nullptr;
+  if (need > 0 && mqa::topk_static_scratch(&ws) != hipSuccess) return MQA_ERR_HIP;
+  return launch_topk_checked(logits, context_lens, max_model_len, k, idx, shape, ws, stream);
 }
 
 int mqa_logits(const uint8_t* q, const uint8_t* k, const float* k_scale, const float* weights,

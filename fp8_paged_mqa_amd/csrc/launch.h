@@ -91,4 +91,9 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream);
 // Enqueue the top-k kernel(s) on `stream`.
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
 
+// Size of the library's static device scratch for the no-allocation top-k, and its
+// device address on the current device (looked up once per device; no allocation).
+size_t topk_static_scratch_bytes();
+hipError_t topk_static_scratch(void** ptr);
+
 }  // namespace mqa

@@ -48,6 +48,8 @@
 // one launch, one workgroup per row, no workspace.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "launch.h"
 
 namespace mqa {
@@ -826,7 +828,32 @@ int compute_units() {
   return n;
 }
 
+// Scratch of the no-allocation entry point: one copy per device, held until the process
+// ends. Host code never uses this name as an address (on the host it is a stand-in, not
+// device memory): topk_static_scratch() looks the device address up once per device.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 }  // namespace
+
+size_t topk_static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t topk_static_scratch(void** ptr) {
+  static std::atomic<void*> per_device[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = per_device[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    per_device[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 size_t topk_workspace_bytes(int64_t rows, int32_t max_model_len) {
   if (max_model_len <= kWide) return 0;

@@ -15,9 +15,9 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa.so")
 
-MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED, MQA_ERR_WORKSPACE, MQA_ERR_HIP = range(6)
+MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED, MQA_ERR_WORKSPACE, MQA_ERR_HIP, MQA_ERR_SCRATCH = range(7)
 
-EXPORTS = ("mqa_paged_logits", "mqa_topk", "mqa_topk_workspace_bytes", "mqa_status_string",
+EXPORTS = ("mqa_paged_logits", "mqa_topk", "mqa_topk_noalloc", "mqa_topk_workspace_bytes", "mqa_status_string",
            "mqa_indexer_k_write", "mqa_logits", "mqa_sparse_mla_decode", "mqa_sparse_mla_workspace_bytes")
 MQA_DTYPE_BF16, MQA_DTYPE_F32 = 0, 1
 
@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
     lib.mqa_paged_logits.restype = ctypes.c_int
     lib.mqa_topk.argtypes = [vp, vp, i32, i32, vp, shp, vp, sz, vp]
     lib.mqa_topk.restype = ctypes.c_int
+    lib.mqa_topk_noalloc.argtypes = [vp, vp, i32, i32, vp, shp, vp]
+    lib.mqa_topk_noalloc.restype = ctypes.c_int
     lib.mqa_topk_workspace_bytes.argtypes = [shp, i32, i32]
     lib.mqa_topk_workspace_bytes.restype = sz
     lib.mqa_status_string.argtypes = [ctypes.c_int]
@@ -126,6 +128,16 @@ def mqa_topk(logits, context_lens, max_model_len, k, idx, shape: mqa_shape, work
                        ctypes.byref(shape), _ptr(workspace), ws_bytes, _stream(stream))
     if check and st != MQA_OK:
         raise MqaError(st, "mqa_topk")
+    return st
+
+
+def mqa_topk_noalloc(logits, context_lens, max_model_len, k, idx, shape: mqa_shape, stream=None,
+                     check: bool = True) -> int:
+    """As mqa_topk, with the library's static device scratch instead of a workspace."""
+    st = _lib.mqa_topk_noalloc(_ptr(logits), _ptr(context_lens), int(max_model_len), int(k), _ptr(idx),
+                               ctypes.byref(shape), _stream(stream))
+    if check and st != MQA_OK:
+        raise MqaError(st, "mqa_topk_noalloc")
     return st
 
 

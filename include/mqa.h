@@ -26,7 +26,8 @@
  *       ctx is read as min(max(ctx, 0), block_table_stride * block_size,
  *       max_model_len); a block-table entry outside [0, num_blocks) yields NaN
  *       logits for the tokens of that block instead of a memory access.
- *   - Calls are reentrant: no mutable global state.
+ *   - Calls are reentrant: no mutable global state, except the static scratch of
+ *     mqa_topk_noalloc (see there).
  */
 #ifndef MQA_H
 #define MQA_H
@@ -47,7 +48,8 @@ enum {
   MQA_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be, or overflows */
   MQA_ERR_UNSUPPORTED = 3, /* a valid shape outside the supported domain (below) */
   MQA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than mqa_topk_workspace_bytes */
-  MQA_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+  MQA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
+  MQA_ERR_SCRATCH = 6      /* mqa_topk_noalloc: the problem needs more than the static scratch */
 };
 
 /*
@@ -141,6 +143,28 @@ int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* wei
 int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model_len,
              int32_t k, int32_t* idx, const mqa_shape* shape, void* workspace,
              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mqa_topk_noalloc - mqa_topk without a workspace argument and without any allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. The result is that of mqa_topk with the
+ * same arguments (the same kernels run); the scratch that mqa_topk takes from its
+ * workspace argument is a static device array of the library instead, 64 MiB on each
+ * device the library runs on, held until the process ends. A problem whose
+ * mqa_topk_workspace_bytes exceeds 64 MiB is rejected with MQA_ERR_SCRATCH before
+ * anything is enqueued (rows longer than 32768 need about 80 KB each, so up to ~800 such
+ * rows per call; shorter rows need none). The call allocates nothing: the array's device
+ * address is looked up once per device (hipGetSymbolAddress) on the first call that needs
+ * it. Every call on a device shares that device's array, which keeps the last call's
+ * contents (each call initialises what it uses, in stream order): calls that overlap in
+ * time on one device - on different streams, or from different threads - race and give
+ * undefined results. Calls in one stream are ordered and safe.
+ * Arguments, layouts and other errors as mqa_topk; MQA_ERR_HIP also reports a failed
+ * symbol lookup.
+ */
+int mqa_topk_noalloc(const float* logits, const int32_t* context_lens, int32_t max_model_len,
+                     int32_t k, int32_t* idx, const mqa_shape* shape, hipStream_t stream);
 
 /*
  * mqa_logits - the same logits over contiguous keys for M query rows with per-row key

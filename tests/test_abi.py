@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(6):
+    for st in range(7):
         assert mqa.mqa_status_string(st)
     assert mqa.mqa_status_string(0) == "ok"
     assert "unknown" in mqa.mqa_status_string(99)
@@ -140,6 +140,33 @@ def test_topk_workspace_alignment_and_size():
     assert call_topk(shape, L=40000, ws=ctypes.c_void_p(0x10000), ws_bytes=need - 1) == mqa.MQA_ERR_WORKSPACE
     assert call_topk(shape, L=40000, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == mqa.MQA_ERR_WORKSPACE
     assert mqa.mqa_topk_workspace_bytes(shape, 32768, 2048) == 0
+
+
+def call_topk_noalloc(shape, L=100, k=2048, ptrs=(FAKE,) * 3):
+    logits, ctx, idx = ptrs
+    return mqa._lib.mqa_topk_noalloc(logits, ctx, L, k, idx,
+                                     ctypes.byref(shape) if shape is not None else None, None)
+
+
+def test_topk_noalloc_host_checks():
+    # the same shape checks as mqa_topk, then the static scratch limit (64 MiB), all
+    # before any HIP call
+    assert call_topk_noalloc(None) == mqa.MQA_ERR_NULL
+    assert call_topk_noalloc(good_shape(block_size=3)) == mqa.MQA_ERR_UNSUPPORTED
+    assert call_topk_noalloc(good_shape(), k=0) == mqa.MQA_ERR_SHAPE
+    assert call_topk_noalloc(good_shape(), k=2049) == mqa.MQA_ERR_UNSUPPORTED
+    big = good_shape(batch=1024, next_n=1, block_table_stride=202752)
+    assert mqa.mqa_topk_workspace_bytes(big, 202752, 2048) > 64 << 20
+    assert call_topk_noalloc(big, L=202752) == mqa.MQA_ERR_SCRATCH
+    ok = good_shape(batch=256, next_n=2, block_table_stride=202752)
+    assert 0 < mqa.mqa_topk_workspace_bytes(ok, 202752, 2048) <= 64 << 20
+    assert call_topk_noalloc(ok, L=202752, ptrs=(None,) * 3) == mqa.MQA_ERR_NULL
+    assert call_topk_noalloc(good_shape(batch=0), ptrs=(None,) * 3) == mqa.MQA_OK
+    odd = ctypes.c_void_p(0x10002)
+    for i in range(3):
+        ptrs = [FAKE] * 3
+        ptrs[i] = odd
+        assert call_topk_noalloc(good_shape(), ptrs=tuple(ptrs)) == mqa.MQA_ERR_UNSUPPORTED, i
 
 
 def test_workspace_size_query():
