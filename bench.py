@@ -1,6 +1,8 @@
 """Throughput of the fp8 paged MQA indexer (logits + top-2048) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--block-size S] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--block-size S]
+                    [--no-cpu-baseline] [--no-workloads]
+    python bench.py --op gather [--workload NAME]   (gather ceiling of the logits' row reads)
     python bench.py --op kwrite [--tokens T]   (the K-cache write alone; not the default line)
     python bench.py --op prefill [--m M --n N --heads H]   (non-paged logits; not the default line)
     python bench.py --op mla   (sparse MLA decode over the selected positions; not the default line)
@@ -9,21 +11,31 @@ One step = mqa_paged_logits + mqa_topk over one batch of the named synthetic wor
 inputs already resident in HBM. Steps are captured into a HIP graph and replayed (the
 indexer runs once per layer per decode step, so serving stacks replay it from graphs;
 eager launches from Python cost more host time than the GPU work). Consecutive steps
-rotate over `--copies` copies of the inputs and outputs, so every step reads buffers
-that the steps in between have evicted from the 256 MB Infinity Cache.
+rotate over copies of the inputs and outputs (up to `--copies`, at least enough that
+~768 MB pass between two uses of one copy), so every step reads buffers that the steps
+in between have evicted from the 256 MB Infinity Cache.
 
 Timed region: exactly K steps (graph replays), bracketed by torch.cuda.synchronize().
 value = indexed KV tokens (sum of context lengths) per second of that region.
 
 The JSON line also carries:
+  step_us       median, p10 and p90 of the mean step time of 24 replays of the rotating
+                steps (HIP events around each replay);
   roofline      the logits kernel (the dominant one) against HBM: algorithmic bytes per
                 launch / its mean launch time, from HIP events on the launch stream around
                 graphs of back-to-back logits launches (same rotation);
   traffic       measured HBM bytes per logits launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
                 scaled by the copy calibration) from the committed profile summary, when
                 that summary was taken on the current kernel source;
-  cpu_baseline  the CPU oracle (float64 numpy) on the same workload on this host's cores;
-                a reported baseline, not a target.
+  gather_ceiling  the measurement probe's pure gather of the same rows in the same order
+                (include/mqa_probe.h) and the logits kernel's time as a fraction of it;
+  workloads     the same protocol on every named workload (the five serving shapes and
+                the context-parallel shard): step time (mean of the timed region, and
+                p50/p10/p90), tokens/s, per-launch logits and top-k times, the logits
+                roofline fraction (algorithmic, and measured-traffic when a profile of the
+                current source exists);
+  cpu_baseline  the CPU oracle (float64 numpy) on the same workload on this host's cores,
+                with the host CPU model; a reported baseline, not a target.
 """
 from __future__ import annotations
 
@@ -263,6 +275,155 @@ def bench_mla(args):
                      "algorithmic_bytes": nbytes, "traffic": None}}), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def input_copies(w, requested):
+    """Enough rotating copies that a step never finds its inputs and outputs in the 256 MB
+    Infinity Cache (at least ~768 MB between two uses of one copy), at most `requested`."""
+    per_step = w.kv_cache.nbytes + 4 * w.rows * w.max_model_len + w.block_tables.nbytes
+    return int(max(2, min(requested, -(-(768 << 20) // max(per_step, 1)))))
+
+
+class Step:
+    """Device copies of one workload and the captured graphs of its step."""
+
+    def __init__(self, w, copies):
+        import torch
+        from fp8_paged_mqa_amd import mqa
+        self.torch, self.mqa, self.w = torch, mqa, w
+        dev = "cuda"
+        self.shape = mqa.make_shape(w.batch, w.next_n, w.heads, w.num_blocks, w.block_tables.shape[1],
+                                    block_size=w.block_size)
+        self.L, self.k, self.C = w.max_model_len, w.k, copies
+        ws_bytes = max(16, mqa.mqa_topk_workspace_bytes(self.shape, self.L, self.k))
+        host = dict(q=torch.from_numpy(w.q), kv=torch.from_numpy(w.kv_cache), w=torch.from_numpy(w.weights),
+                    ctx=torch.from_numpy(w.context_lens.astype(np.int32)),
+                    bt=torch.from_numpy(w.block_tables.astype(np.int32)))
+        self.copies = []
+        for _ in range(copies):
+            c = {key: t.to(dev) for key, t in host.items()}
+            c["out"] = torch.empty((w.rows, self.L), dtype=torch.float32, device=dev)
+            c["idx"] = torch.empty((w.rows, self.k), dtype=torch.int32, device=dev)
+            c["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            self.copies.append(c)
+
+    def logits(self, c):
+        self.mqa.mqa_paged_logits(c["q"], c["kv"], c["w"], c["ctx"], c["bt"], self.L, c["out"], self.shape)
+
+    def topk(self, c):
+        self.mqa.mqa_topk(c["out"], c["ctx"], self.L, self.k, c["idx"], self.shape, c["ws"])
+
+    def step(self, c):
+        self.logits(c)
+        self.topk(c)
+
+    def capture(self, fn, n):
+        g = self.torch.cuda.CUDAGraph()
+        with self.torch.cuda.graph(g):
+            for i in range(n):
+                fn(self.copies[i % self.C])
+        return g
+
+    def replay_us(self, g, per_replay, reps):
+        """Per-replay mean time of one unit (us), from HIP events on the launch stream around
+        each replay, for `reps` back-to-back replays."""
+        torch = self.torch
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            g.replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 / per_replay for i in range(reps)])
+
+
+def measure(w, steps, warmup, copies, tag):
+    """Timed region of exactly `steps` steps, then per-step and per-launch distributions."""
+    import torch
+    st = Step(w, input_copies(w, copies))
+    C = st.C
+    for i in range(4):                 # eager warmup (also loads the code objects)
+        st.step(st.copies[i % C])
+    torch.cuda.synchronize()
+    g_steps = st.capture(st.step, C)   # C steps, one per input copy
+    rem = steps % C
+    g_rem = st.capture(st.step, rem) if rem else None
+    for _ in range(max(1, warmup // C)):
+        g_steps.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps // C):
+        g_steps.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    # Distribution: each sample is the mean step time of one replay of C rotating steps.
+    dist = st.replay_us(g_steps, C, 24)
+    t_logits = float(np.mean(st.replay_us(st.capture(st.logits, C), C, 8)))
+    t_topk = float(np.mean(st.replay_us(st.capture(st.topk, C), C, 8)))
+    bytes_logits, bytes_topk = algorithmic_bytes(w)
+    frac = bytes_logits / (t_logits * 1e-6) / 1e9 / HBM_PEAK_GBPS
+    traffic = traffic_from_profile("logits", tag, source_digest(LOGITS_SRC))
+    med = float(np.median(dist))
+    out = {
+        "ms_per_step": ms_per_step,
+        "step_us_p50": med, "step_us_p10": float(np.percentile(dist, 10)),
+        "step_us_p90": float(np.percentile(dist, 90)),
+        "tokens_per_s": w.sum_ctx / (ms_per_step * 1e-3),
+        "kernels_us": {"logits": t_logits, "topk": t_topk},
+        "logits_roofline_frac": frac,
+        "logits_algorithmic_bytes": bytes_logits,
+        "logits_traffic_bytes": traffic,
+        "logits_traffic_frac": None if traffic is None else traffic / (t_logits * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        "hbm_frac_step": (bytes_logits + bytes_topk) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "input_copies": C,
+    }
+    return st, out
+
+
+def gather_rows(w):
+    """Cache rows the logits kernel reads, in the order it visits them (request-major,
+    position ascending)."""
+    S = w.block_size
+    rows = []
+    for b in range(w.batch):
+        t = np.arange(int(w.context_lens[b]), dtype=np.int64)
+        rows.append(w.block_tables[b][t // S].astype(np.int64) * S + t % S)
+    return np.concatenate(rows).astype(np.int32) if rows else np.zeros(0, np.int32)
+
+
+def gather_ceiling(st):
+    """The probe's gather of the rows the logits kernel reads (same copies, same rotation),
+    best over 1, 2 and 4 workgroups of 4 waves per CU and 2 or 4 stages in flight."""
+    torch, mqa, w = st.torch, st.mqa, st.w
+    rows = torch.from_numpy(gather_rows(w)).cuda()
+    best, tried = None, {}
+    for gpc in (1, 2, 4):
+        for depth in (2, 4):
+            sink = torch.empty(mqa.mqa_probe_gather_sink_words(gpc), dtype=torch.int32, device="cuda")
+            fn = lambda c, gpc=gpc, sink=sink, depth=depth: mqa.mqa_probe_gather(c["kv"], rows, gpc, sink, depth)  # noqa: E731
+            us = float(np.mean(st.replay_us(st.capture(fn, st.C), st.C, 8)))
+            tried[f"{gpc}x{depth}"] = us
+            if best is None or us < best[0]:
+                best = (us, gpc, depth)
+    n = int(rows.numel())
+    return {"us": best[0], "groups_per_cu": best[1], "stages_in_flight": best[2], "rows": n,
+            "gbps_algorithmic": (ROW_BYTES + 4) * n / (best[0] * 1e-6) / 1e9,
+            "us_by_groups_x_stages": tried}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,7 +435,9 @@ def main():
     ap.add_argument("--block-size", type=int, default=1,
                     help="tokens per KV block (1: the pages' layout; the default line uses 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="step", choices=["step", "kwrite", "prefill", "mla"])
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-workload table (every named workload, same protocol)")
+    ap.add_argument("--op", default="step", choices=["step", "kwrite", "prefill", "mla", "gather"])
     ap.add_argument("--m", type=int, default=4096, help="query rows for --op prefill")
     ap.add_argument("--n", type=int, default=8192, help="keys for --op prefill")
     ap.add_argument("--heads", type=int, default=32, help="heads for --op prefill")
@@ -298,134 +461,86 @@ def main():
 
     import torch
     sys.path.insert(0, ROOT)
-    from fp8_paged_mqa_amd import mqa, workloads
+    from fp8_paged_mqa_amd import workloads
 
-    w = workloads.make_named(args.workload or workloads.DEFAULT_WORKLOAD, poison_unused=False,
-                             block_size=args.block_size)
+    name = args.workload or workloads.DEFAULT_WORKLOAD
+    w = workloads.make_named(name, poison_unused=False, block_size=args.block_size)
     print(f"[bench] {w.name}: sum_ctx={w.sum_ctx} pool={w.num_blocks}", file=sys.stderr, flush=True)
-    dev = "cuda"
-    shape = mqa.make_shape(w.batch, w.next_n, w.heads, w.num_blocks, w.block_tables.shape[1],
-                           block_size=w.block_size)
-    L, k = w.max_model_len, w.k
-    C = max(1, args.copies)
-    ws_bytes = max(1, mqa.mqa_topk_workspace_bytes(shape, L, k))
-    copies = []
-    for _ in range(C):
-        copies.append(dict(
-            q=torch.from_numpy(w.q).to(dev), kv=torch.from_numpy(w.kv_cache).to(dev),
-            w=torch.from_numpy(w.weights).to(dev),
-            ctx=torch.from_numpy(w.context_lens.astype(np.int32)).to(dev),
-            bt=torch.from_numpy(w.block_tables.astype(np.int32)).to(dev),
-            out=torch.empty((w.rows, L), dtype=torch.float32, device=dev),
-            idx=torch.empty((w.rows, k), dtype=torch.int32, device=dev),
-            ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
-
-    def logits(c):
-        mqa.mqa_paged_logits(c["q"], c["kv"], c["w"], c["ctx"], c["bt"], L, c["out"], shape)
-
-    def topk(c):
-        mqa.mqa_topk(c["out"], c["ctx"], L, k, c["idx"], shape, c["ws"])
-
-    def step(c):
-        logits(c)
-        topk(c)
-
-    def capture(fn, n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(copies[i % C])
-        return g
-
-    # Eager warmup (also loads the code objects), then the graphs.
-    for i in range(4):
-        step(copies[i % C])
-    torch.cuda.synchronize()
-    g_steps = capture(step, C)                 # C steps, one per input copy
-    rem = args.steps % C
-    g_rem = capture(step, rem) if rem else None
-    for _ in range(max(1, args.warmup // C)):
-        g_steps.replay()
-    torch.cuda.synchronize()
-
-    # Timed region: exactly K steps.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps // C):
-        g_steps.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # Per-kernel mean launch time: HIP events on the launch stream around graphs of
-    # back-to-back launches of one kernel.
-    def per_launch_us(fn, reps=8):
-        g = capture(fn, C)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (reps * C)
-
-    t_logits = per_launch_us(logits)
-    t_topk = per_launch_us(topk)
+    tag = w.name.split(":")[0] + (f"_bs{w.block_size}" if w.block_size > 1 else "")
+    st, m = measure(w, args.steps, args.warmup, args.copies, tag)
+    ceiling = gather_ceiling(st)
+    if args.op == "gather":
+        print(json.dumps({
+            "metric": "gather ceiling: 132-byte cache rows the paged logits kernel reads, in its order",
+            "value": ceiling["gbps_algorithmic"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+            "data": "synthetic", "config": {"workload": w.name, "block_size": w.block_size},
+            "gather": ceiling, "logits_us": m["kernels_us"]["logits"],
+            "logits_frac_of_ceiling": ceiling["us"] / m["kernels_us"]["logits"]}), flush=True)
+        return
 
     # Host-launched steps (no graph), for reference.
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     n_eager = min(args.steps, 50)
     for i in range(n_eager):
-        step(copies[i % C])
+        st.step(st.copies[i % st.C])
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t1) * 1e3 / n_eager
 
     if args.calibrate_copy_mib > 0:  # a plain copy of known size, for counter calibration
         nbytes = args.calibrate_copy_mib << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
 
-    bytes_logits, bytes_topk = algorithmic_bytes(w)
+    bytes_logits = m["logits_algorithmic_bytes"]
+    t_logits = m["kernels_us"]["logits"]
     achieved = bytes_logits / (t_logits * 1e-6) / 1e9
-    tag = w.name.split(":")[0] + (f"_bs{w.block_size}" if w.block_size > 1 else "")
-    traffic = traffic_from_profile("logits", tag, source_digest(LOGITS_SRC))
-    value = w.sum_ctx / (ms_per_step * 1e-3)
-    step_gbps = (bytes_logits + bytes_topk) / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
-        "value": value,
+        "value": m["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8e4m3fn->f16 mfma, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "next_n": w.next_n, "heads": w.heads,
-                   "head_dim": 128, "block_size": w.block_size, "max_model_len": L, "k": k,
-                   "sum_ctx": w.sum_ctx, "pool_rows": w.num_blocks, "input_copies": C,
+                   "head_dim": 128, "block_size": w.block_size, "max_model_len": st.L, "k": st.k,
+                   "sum_ctx": w.sum_ctx, "pool_rows": w.num_blocks, "input_copies": st.C,
                    "timing": "HIP graph replay of the step"},
-        "hbm_frac_step": step_gbps / HBM_PEAK_GBPS,
-        "kernels_us": {"logits": t_logits, "topk": t_topk},
+        "step_us": {"p50": m["step_us_p50"], "p10": m["step_us_p10"], "p90": m["step_us_p90"],
+                    "sample": f"24 replays of {st.C} rotating steps, HIP events per replay"},
+        "hbm_frac_step": m["hbm_frac_step"],
+        "kernels_us": m["kernels_us"],
         "eager_ms_per_step": eager_ms,
+        "gather_ceiling": {**ceiling, "logits_frac_of_ceiling": ceiling["us"] / t_logits},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "kernel": "paged_logits_kernel",
-                     "algorithmic_bytes": bytes_logits, "traffic": traffic},
+                     "algorithmic_bytes": bytes_logits, "traffic": m["logits_traffic_bytes"]},
     }
+    del st
+    torch.cuda.empty_cache()
+    if not args.no_workloads:
+        table = {}
+        for other in workloads.WORKLOADS:
+            wo = w if other == name and args.block_size == 1 else workloads.make_named(other, poison_unused=False)
+            print(f"[bench] workload {other}: sum_ctx={wo.sum_ctx}", file=sys.stderr, flush=True)
+            st_o, mo = measure(wo, args.steps, args.warmup, args.copies, other)
+            table[other] = {k: v for k, v in mo.items() if k != "logits_algorithmic_bytes"}
+            del st_o
+            torch.cuda.empty_cache()
+        result["workloads"] = table
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"]["cpu_model"] = cpu_model()
     print(json.dumps(result), flush=True)
 
 

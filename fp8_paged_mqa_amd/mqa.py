@@ -20,6 +20,8 @@ MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED, MQA_ERR_WORKSPACE, MQA
 EXPORTS = ("mqa_paged_logits", "mqa_topk", "mqa_topk_noalloc", "mqa_topk_workspace_bytes", "mqa_status_string",
            "mqa_indexer_k_write", "mqa_logits", "mqa_sparse_mla_decode", "mqa_sparse_mla_workspace_bytes")
 MQA_DTYPE_BF16, MQA_DTYPE_F32 = 0, 1
+# The measurement probe (include/mqa_probe.h): not part of the operation.
+PROBE_EXPORTS = ("mqa_probe_gather", "mqa_probe_gather_sink_words")
 
 
 class mqa_shape(ctypes.Structure):
@@ -67,6 +69,10 @@ def _load() -> ctypes.CDLL:
     lib.mqa_sparse_mla_decode.restype = ctypes.c_int
     lib.mqa_sparse_mla_workspace_bytes.argtypes = [mshp]
     lib.mqa_sparse_mla_workspace_bytes.restype = sz
+    lib.mqa_probe_gather_sink_words.argtypes = [i32]
+    lib.mqa_probe_gather_sink_words.restype = sz
+    lib.mqa_probe_gather.argtypes = [vp, i64, vp, i64, i32, i32, vp, sz, vp]
+    lib.mqa_probe_gather.restype = ctypes.c_int
     return lib
 
 
@@ -198,6 +204,21 @@ def mqa_sparse_mla_decode(q, q_scale, kv_cache, kv_scale, indices, block_tables,
                                     _ptr(workspace), ws_bytes, _stream(stream))
     if check and st != MQA_OK:
         raise MqaError(st, "mqa_sparse_mla_decode")
+    return st
+
+
+def mqa_probe_gather_sink_words(groups_per_cu: int) -> int:
+    return int(_lib.mqa_probe_gather_sink_words(int(groups_per_cu)))
+
+
+def mqa_probe_gather(kv_cache, rows, groups_per_cu, sink, stages_in_flight=2, stream=None, check: bool = True) -> int:
+    """Measurement probe: gathers the 132-byte cache rows listed in rows (int32 [n]) the
+    way the paged logits kernel reads them, folding them into sink (int32)."""
+    st = _lib.mqa_probe_gather(_ptr(kv_cache), int(kv_cache.numel() // 132), _ptr(rows), int(rows.numel()),
+                               int(groups_per_cu), int(stages_in_flight), _ptr(sink), int(sink.numel()),
+                               _stream(stream))
+    if check and st != 0:
+        raise RuntimeError(f"mqa_probe_gather: status {st}")
     return st
 
 

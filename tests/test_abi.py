@@ -13,23 +13,46 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mqa.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mqa_\w+)\s*\(", text, flags=re.M)))
 
 
+def all_headers():
+    inc = os.path.join(ROOT, "include")
+    return sorted(os.path.join(inc, f) for f in os.listdir(inc) if f.endswith(".h"))
+
+
 def test_header_declares_the_binding_names():
     assert declared_functions() == sorted(mqa.EXPORTS)
+    probe = os.path.join(ROOT, "include", "mqa_probe.h")
+    assert declared_functions(probe) == sorted(mqa.PROBE_EXPORTS)
 
 
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", mqa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
-    for name in declared_functions():
+    names = [n for h in all_headers() for n in declared_functions(h)]
+    assert len(names) == len(mqa.EXPORTS) + len(mqa.PROBE_EXPORTS)
+    for name in names:
         assert name in exported, name
         assert hasattr(mqa._lib, name)
+
+
+def test_probe_host_checks():
+    # rejected before any HIP call
+    sink = ctypes.c_void_p(0x10000)
+    probe = mqa._lib.mqa_probe_gather
+    assert probe(FAKE, 10, FAKE, -1, 2, 2, sink, 1 << 20, None) == 2
+    assert probe(FAKE, 0, FAKE, 5, 2, 2, sink, 1 << 20, None) == 2
+    assert probe(FAKE, 10, FAKE, 5, 0, 2, sink, 1 << 20, None) == 3
+    assert probe(FAKE, 10, FAKE, 5, 9, 2, sink, 1 << 20, None) == 3
+    assert probe(FAKE, 10, FAKE, 5, 2, 3, sink, 1 << 20, None) == 3
+    assert probe(None, 10, FAKE, 5, 2, 2, sink, 1 << 20, None) == 1
+    assert probe(ctypes.c_void_p(0x10002), 10, FAKE, 5, 2, 2, sink, 1 << 20, None) == 3
+    assert probe(FAKE, 10, FAKE, 0, 2, 2, sink, 0, None) == 0
 
 
 def test_status_strings():
