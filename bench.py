@@ -304,7 +304,7 @@ class Step:
         self.shape = mqa.make_shape(w.batch, w.next_n, w.heads, w.num_blocks, w.block_tables.shape[1],
                                     block_size=w.block_size)
         self.L, self.k, self.C = w.max_model_len, w.k, copies
-        ws_bytes = max(16, mqa.mqa_topk_workspace_bytes(self.shape, self.L, self.k))
+        ws_bytes = max(16, mqa.mqa_topk_workspace_bytes(self.shape, self.L, self.k))  # zero-filled once
         host = dict(q=torch.from_numpy(w.q), kv=torch.from_numpy(w.kv_cache), w=torch.from_numpy(w.weights),
                     ctx=torch.from_numpy(w.context_lens.astype(np.int32)),
                     bt=torch.from_numpy(w.block_tables.astype(np.int32)))
@@ -313,7 +313,7 @@ class Step:
             c = {key: t.to(dev) for key, t in host.items()}
             c["out"] = torch.empty((w.rows, self.L), dtype=torch.float32, device=dev)
             c["idx"] = torch.empty((w.rows, self.k), dtype=torch.int32, device=dev)
-            c["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            c["ws"] = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
             self.copies.append(c)
 
     def logits(self, c):

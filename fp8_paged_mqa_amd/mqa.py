@@ -235,7 +235,7 @@ class Indexer:
         self.logits = torch.empty((rows, self.max_model_len), dtype=torch.float32, device=device)
         self.idx = torch.empty((rows, self.k), dtype=torch.int32, device=device)
         nbytes = mqa_topk_workspace_bytes(self.shape, self.max_model_len, self.k)
-        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        self.workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)  # zero before first use
 
     def __call__(self, q, kv_cache, weights, context_lens, block_tables, stream=None):
         mqa_paged_logits(q, kv_cache, weights, context_lens, block_tables, self.max_model_len,

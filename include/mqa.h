@@ -134,9 +134,12 @@ int mqa_paged_logits(const uint8_t* q, const uint8_t* kv_cache, const float* wei
  *   idx             int32  [B*N, k]   4-byte aligned
  *   workspace       device scratch of at least mqa_topk_workspace_bytes(shape,
  *                   max_model_len, k) bytes, 16-byte aligned (may be NULL when that
- *                   size is 0, i.e. max_model_len <= 32768); contents on entry do not
- *                   matter, the call initialises what it uses, in stream order. Calls
- *                   that overlap in time must not share a workspace.
+ *                   size is 0, i.e. max_model_len <= 32768). It must hold zeros before
+ *                   its first use (fill it once, e.g. hipMemset or torch.zeros, outside
+ *                   any captured graph); every call returns it to zero before it ends,
+ *                   in stream order, so the same workspace serves any number of calls of
+ *                   any shape that fits it, captured into graphs or not. Calls that
+ *                   overlap in time must not share a workspace.
  * Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_SHAPE, MQA_ERR_UNSUPPORTED,
  * MQA_ERR_WORKSPACE or MQA_ERR_HIP.
  */
@@ -151,15 +154,16 @@ int mqa_topk(const float* logits, const int32_t* context_lens, int32_t max_model
  * serving loops, harnesses that forbid hipMalloc. The result is that of mqa_topk with the
  * same arguments (the same kernels run); the scratch that mqa_topk takes from its
  * workspace argument is a static device array of the library instead, 64 MiB on each
- * device the library runs on, held until the process ends. A problem whose
- * mqa_topk_workspace_bytes exceeds 64 MiB is rejected with MQA_ERR_SCRATCH before
- * anything is enqueued (rows longer than 32768 need about 80 KB each, so up to ~800 such
- * rows per call; shorter rows need none). The call allocates nothing: the array's device
- * address is looked up once per device (hipGetSymbolAddress) on the first call that needs
- * it. Every call on a device shares that device's array, which keeps the last call's
- * contents (each call initialises what it uses, in stream order): calls that overlap in
- * time on one device - on different streams, or from different threads - race and give
- * undefined results. Calls in one stream are ordered and safe.
+ * device the library runs on, zero when the library is loaded and held until the process
+ * ends. A problem whose mqa_topk_workspace_bytes exceeds 64 MiB is rejected with
+ * MQA_ERR_SCRATCH before anything is enqueued (with max_model_len > 32768 every row needs
+ * about 80 KB, so up to ~800 rows per call; with max_model_len <= 32768 none is needed).
+ * The call allocates nothing: the array's device address is looked up once per device
+ * (hipGetSymbolAddress) on the first call that needs it. Every call on a device shares
+ * that device's array and, like mqa_topk with its workspace, returns it to zero before it
+ * ends: calls that overlap in time on one device - on different streams, or from
+ * different threads - race and give undefined results. Calls in one stream are ordered
+ * and safe.
  * Arguments, layouts and other errors as mqa_topk; MQA_ERR_HIP also reports a failed
  * symbol lookup.
  */

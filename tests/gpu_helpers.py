@@ -55,7 +55,7 @@ def run_gpu(wl, k=None, poison=True):
     out = torch.full((wl.rows, L), float("nan") if poison else 0.0, dtype=torch.float32, device="cuda")
     idx = torch.full((wl.rows, k), -7, dtype=torch.int32, device="cuda")
     nbytes = mqa.mqa_topk_workspace_bytes(shape, L, k)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")  # zero before first use
     mqa.mqa_paged_logits(d["q"], d["kv"], d["w"], d["ctx"], d["bt"], L, out, shape)
     mqa.mqa_topk(out, d["ctx"], L, k, idx, shape, ws)
     torch.cuda.synchronize()

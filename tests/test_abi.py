@@ -154,7 +154,7 @@ def test_empty_batch_is_a_no_op():
 
 
 def test_topk_workspace_alignment_and_size():
-    # rows longer than 32768 need the workspace: missing, short or not 16-byte aligned
+    # max_model_len above 32768 needs the workspace: missing, short or not 16-byte aligned
     # are all MQA_ERR_WORKSPACE, checked before any pointer is used
     shape = good_shape(block_table_stride=40000)
     need = mqa.mqa_topk_workspace_bytes(shape, 40000, 2048)
@@ -163,6 +163,7 @@ def test_topk_workspace_alignment_and_size():
     assert call_topk(shape, L=40000, ws=ctypes.c_void_p(0x10000), ws_bytes=need - 1) == mqa.MQA_ERR_WORKSPACE
     assert call_topk(shape, L=40000, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == mqa.MQA_ERR_WORKSPACE
     assert mqa.mqa_topk_workspace_bytes(shape, 32768, 2048) == 0
+    assert mqa.mqa_topk_workspace_bytes(shape, 32769, 2048) > 0
 
 
 def call_topk_noalloc(shape, L=100, k=2048, ptrs=(FAKE,) * 3):
@@ -181,7 +182,7 @@ def test_topk_noalloc_host_checks():
     big = good_shape(batch=1024, next_n=1, block_table_stride=202752)
     assert mqa.mqa_topk_workspace_bytes(big, 202752, 2048) > 64 << 20
     assert call_topk_noalloc(big, L=202752) == mqa.MQA_ERR_SCRATCH
-    ok = good_shape(batch=256, next_n=2, block_table_stride=202752)
+    ok = good_shape(batch=128, next_n=4, block_table_stride=202752)
     assert 0 < mqa.mqa_topk_workspace_bytes(ok, 202752, 2048) <= 64 << 20
     assert call_topk_noalloc(ok, L=202752, ptrs=(None,) * 3) == mqa.MQA_ERR_NULL
     assert call_topk_noalloc(good_shape(batch=0), ptrs=(None,) * 3) == mqa.MQA_OK

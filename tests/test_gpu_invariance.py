@@ -170,7 +170,7 @@ def test_graph_replay_matches_eager():
     L, k = case.max_model_len, case.k
     out = torch.empty((case.rows, L), dtype=torch.float32, device="cuda")
     idx = torch.empty((case.rows, k), dtype=torch.int32, device="cuda")
-    ws = torch.empty(max(1, mqa.mqa_topk_workspace_bytes(shape, L, k)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(1, mqa.mqa_topk_workspace_bytes(shape, L, k)), dtype=torch.uint8, device="cuda")
 
     def step():
         mqa.mqa_paged_logits(d["q"], d["kv"], d["w"], d["ctx"], d["bt"], L, out, shape)

@@ -1,11 +1,11 @@
 """mqa_topk on crafted logit rows, one call per path (every row fits one workgroup when
-max_model_len <= 8192, with 8 values per thread, or <= 32768, with 32; longer rows take
-the chunked path), compared as sets with the oracle's selection (larger first, ties by
-lower position, -0.0 equal to +0.0).
+max_model_len <= 8192, with 8 values per thread, or <= 32768, with 32; beyond, rows longer
+than 32768 take the chunked path inside the same launch as the whole rows), compared as
+sets with the oracle's selection (larger first, ties by lower position, -0.0 equal to +0.0).
 
 The rows are chosen to reach each branch of the selection: spread values (linear bins),
 few distinct values (a threshold bin of thousands of elements, refined by radix digits;
-beyond 8192 elements the long path refines from the row itself), a constant row (a single
+beyond 8192 candidates the chunked path refines from the row itself), a constant row (a single
 bin), signed zeros, infinities and a spread that overflows (top-key bins), a narrow
 band around 1e6, a log-uniform spread over 60 decades, subnormals, and rows holding
 NaNs. The oracle orders NaN below everything; the header fixes the kernel's order for
@@ -73,8 +73,9 @@ def bit_order_topk(vals, k):
     return np.sort(order[:min(k, u.size)])
 
 
-def run_case(L, k, specs, seed):
-    """specs: list of (kind, nv). One call to mqa_topk over all rows."""
+def run_case(L, k, specs, seed, ws=None):
+    """specs: list of (kind, nv). One call to mqa_topk over all rows (with the given
+    workspace, else a fresh zero-filled one)."""
     rng = np.random.default_rng(seed)
     rows = len(specs)
     logits = np.full((rows, L), np.nan, np.float32)  # beyond nv: never read as a value
@@ -86,7 +87,9 @@ def run_case(L, k, specs, seed):
     d_ctx = torch.from_numpy(ctx).cuda()
     idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
     nbytes = mqa.mqa_topk_workspace_bytes(shape, L, k)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")  # zero before first use
+    assert ws.numel() >= nbytes
     mqa.mqa_topk(d_logits, d_ctx, L, k, idx, shape, ws)
     torch.cuda.synchronize()
     got = idx.cpu().numpy()
@@ -124,3 +127,23 @@ def test_topk_long_rows(k):
     specs = [(kind, nv) for kind in KINDS for nv in nvs]
     say(f"[gpu] topk crafted rows L=40000 k={k} rows={len(specs)}")
     run_case(40000, k, specs, seed=7100 + k)
+
+
+def test_topk_workspace_reused_and_left_zero():
+    """One workspace serves a sequence of calls of different shapes (its layout moves with
+    the row count): chunked rows of every kind, whole threshold bins, refinement over the
+    row, trivial rows. Every call is checked, and after each the workspace holds zeros
+    again, as the next call requires."""
+    seq = [
+        (40000, 2048, [(kind, nv) for kind in KINDS for nv in (5, 8193, 40000)], 7300),
+        (52000, 100, [(kind, 52000) for kind in KINDS], 7301),
+        (202752, 2048, [("normal", 202752), ("const", 150000), ("few", 99999), ("zeros", 3)], 7302),
+        (33000, 2048, [(kind, nv) for kind in KINDS for nv in (2049, 32769, 33000)], 7303),
+    ]
+    need = max(mqa.mqa_topk_workspace_bytes(mqa.make_shape(len(sp), 1, 64, L, L), L, k) for L, k, sp, _ in seq)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for L, k, specs, seed in seq:
+        say(f"[gpu] topk reused workspace L={L} k={k} rows={len(specs)}")
+        run_case(L, k, specs, seed, ws=ws)
+        nz = int(torch.count_nonzero(ws).item())
+        assert nz == 0, f"L={L} k={k}: {nz} workspace bytes left nonzero"

@@ -49,7 +49,7 @@ def test_noalloc_matches_workspace_entry_point(calls):
         want = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
         got = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
         nbytes = mqa.mqa_topk_workspace_bytes(shape, L, k)
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
         _call(mqa._lib.mqa_topk_noalloc, logits, ctx_d, L, k, got, shape)
         _call(mqa._lib.mqa_topk, logits, ctx_d, L, k, want, shape, ctypes.c_void_p(ws.data_ptr()),
               ctypes.c_size_t(ws.numel()))
