@@ -231,7 +231,7 @@ def bench_mla(args):
         shape = mqa.mla_shape_of(q, kv, bt, idx, case.next_n)
         nbytes = mqa.mqa_sparse_mla_workspace_bytes(shape)
         copies.append(dict(q=q, kv=kv, idx=idx, bt=bt, shape=shape,
-                           ws=torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev),
+                           ws=torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev),
                            out=torch.empty((case.rows, 16, 512), dtype=torch.float32, device=dev),
                            lse=torch.empty((case.rows, 16), dtype=torch.float32, device=dev)))
     def run(c):

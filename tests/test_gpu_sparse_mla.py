@@ -35,7 +35,7 @@ def run_gpu(case):
     lse = torch.full((case.rows, 16), float("nan"), dtype=torch.float32, device="cuda")
     shape = mqa.mla_shape_of(q, kv, bt, idx, case.next_n)
     nbytes = mqa.mqa_sparse_mla_workspace_bytes(shape)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda") if nbytes else None
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda") if nbytes else None
     mqa.mqa_sparse_mla_decode(q, case.q_scale, kv, case.kv_scale, idx, bt, case.sm_scale, out, lse,
                               shape=shape, workspace=ws)
     torch.cuda.synchronize()
@@ -147,7 +147,7 @@ def test_sparse_mla_graph_replay_matches_eager():
     idx, bt = _dev(case.indices), _dev(case.block_tables)
     shape = mqa.mla_shape_of(q, kv, bt, idx, case.next_n)
     nbytes = mqa.mqa_sparse_mla_workspace_bytes(shape)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     out = torch.empty((case.rows, 16, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((case.rows, 16), dtype=torch.float32, device="cuda")
     run = lambda s=None: mqa.mqa_sparse_mla_decode(q, case.q_scale, kv, case.kv_scale, idx, bt,  # noqa: E731
@@ -168,3 +168,29 @@ def test_sparse_mla_graph_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+
+
+def test_sparse_mla_workspace_reused():
+    """One workspace serves a sequence of calls of different shapes (each call rewrites the
+    partial states it reads; nothing may carry over from the call before)."""
+    seq = [(3, 3, [3000, 2049, 2048], 2048, 1, 520), (1, 1, [5000], 2048, 64, 521), (4, 2, [1000, 333, 64, 65], 333, 1, 522),
+           (3, 3, [3000, 2049, 2048], 2048, 1, 523)]
+    cases = [wl.make_mla_case(batch=B, next_n=N, ctx=ctx, topk=topk, block_size=S, seed=sd)
+             for B, N, ctx, topk, S, sd in seq]
+    need = 16
+    for case in cases:
+        q, kv, idx, bt = _dev(case.q), _dev(case.kv_cache), _dev(case.indices), _dev(case.block_tables)
+        need = max(need, mqa.mqa_sparse_mla_workspace_bytes(mqa.mla_shape_of(q, kv, bt, idx, case.next_n)))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for n, case in enumerate(cases):
+        q, kv = _dev(case.q), _dev(case.kv_cache)
+        idx, bt = _dev(case.indices.astype(np.int32)), _dev(case.block_tables.astype(np.int32))
+        out = torch.full((case.rows, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((case.rows, 16), float("nan"), dtype=torch.float32, device="cuda")
+        shape = mqa.mla_shape_of(q, kv, bt, idx, case.next_n)
+        say(f"[gpu] sparse mla reused workspace call {n}: rows={case.rows} topk={case.topk}")
+        mqa.mqa_sparse_mla_decode(q, case.q_scale, kv, case.kv_scale, idx, bt, case.sm_scale, out, lse,
+                                  shape=shape, workspace=ws)
+        torch.cuda.synchronize()
+        check(case, out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), *oracle_of(case),
+              f"reused workspace call {n}")
