@@ -4,6 +4,11 @@
 
 Every call recompiles. Objects go to fp8_paged_mqa_amd/_build/, the library to
 fp8_paged_mqa_amd/libmqa.so.
+
+build(out_dir=D, sanitize=True) builds a second copy into D with AddressSanitizer and
+UndefinedBehaviorSanitizer on the host code only (the host checks of the C ABI); the GPU
+code is compiled as usual. That copy is for host-side test drivers, never for loading
+into Python.
 """
 from __future__ import annotations
 
@@ -26,6 +31,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
 # Packed fp32 VALU ops (v_pk_*_f32) are kept out of the generated code.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
+# Host-only sanitizers: each -fsanitize= is preceded by -Xarch_host so that no GPU code is
+# instrumented.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
 
 
 def _run(cmd):
@@ -35,24 +44,29 @@ def _run(cmd):
     return r
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, out_dir: str | None = None, sanitize: bool = False) -> str:
+    """Compiles every source and links libmqa.so; returns the library's path. With out_dir
+    the objects and the library go there instead of the package."""
+    obj_dir = OBJ if out_dir is None else os.path.join(out_dir, "obj")
+    lib = LIB if out_dir is None else os.path.join(out_dir, "libmqa.so")
+    extra = SANITIZE if sanitize else []
+    os.makedirs(obj_dir, exist_ok=True)
     jobs = []
     for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
-        obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-        jobs.append([HIPCC, *COMMON, *DEVICE, "-c", src, "-o", obj])
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        jobs.append([HIPCC, *COMMON, *DEVICE, *extra, "-c", src, "-o", obj])
     for src in sorted(glob.glob(os.path.join(CSRC, "*.cpp"))):
-        obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-        jobs.append([HIPCC, *COMMON, "-c", src, "-o", obj])
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        jobs.append([HIPCC, *COMMON, *extra, "-c", src, "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         for r in ex.map(_run, jobs):
             if verbose and (r.stdout or r.stderr):
                 print(r.stdout, r.stderr, file=sys.stderr)
     objs = [j[-1] for j in jobs]
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *extra, *objs, "-o", tmp])
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
