@@ -30,7 +30,7 @@ The JSON line also carries:
   gather_ceiling  the measurement probe's pure gather of the same rows in the same order
                 (include/mqa_probe.h) and the logits kernel's time as a fraction of it;
   workloads     the same protocol on every named workload (the five serving shapes and
-                the context-parallel shard): step time (mean of the timed region, and
+                the context-parallel shard) at the run's block size: step time (mean of the timed region, and
                 p50/p10/p90), tokens/s, per-launch logits and top-k times, the logits
                 roofline fraction (algorithmic, and measured-traffic when a profile of the
                 current source exists);
@@ -531,10 +531,11 @@ def main():
     if not args.no_workloads:
         table = {}
         for other in workloads.WORKLOADS:
-            wo = w if other == name and args.block_size == 1 else workloads.make_named(other, poison_unused=False)
+            wo = w if other == name else workloads.make_named(other, poison_unused=False, block_size=args.block_size)
             print(f"[bench] workload {other}: sum_ctx={wo.sum_ctx}", file=sys.stderr, flush=True)
             st_o, mo = measure(wo, args.steps, args.warmup, args.copies, other)
             table[other] = {k: v for k, v in mo.items() if k != "logits_algorithmic_bytes"}
+            table[other]["block_size"] = wo.block_size
             del st_o
             torch.cuda.empty_cache()
         result["workloads"] = table
