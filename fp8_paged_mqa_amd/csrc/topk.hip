@@ -532,13 +532,31 @@ __device__ void select_row(const Params& p, int r, int nv, Full<T, CAP>& sh) {
   }
 }
 
+// Whole-row select with the fewest values per thread that hold the row: a phase costs
+// about one instruction per value a thread holds, and rows shorter than the kernel's
+// longest (clamped loads past nv only repeat the last value) need not pay for it. MAXPER is
+// the longest form a kernel needs.
+template <int T, int CAP, int MAXPER>
+__device__ void select_row_fit(const Params& p, int r, int nv, Full<T, CAP>& sh) {
+  if (nv <= 4 * T) {  // uniform, like every branch here
+    select_row<T, CAP, 4>(p, r, nv, sh);
+  } else if (MAXPER <= 8 || nv <= 8 * T) {
+    select_row<T, CAP, 8>(p, r, nv, sh);
+  } else if constexpr (MAXPER > 8) {
+    if (nv <= 16 * T)
+      select_row<T, CAP, 16>(p, r, nv, sh);
+    else
+      select_row<T, CAP, MAXPER>(p, r, nv, sh);
+  }
+}
+
 // max_model_len <= kRowLen: one launch, workgroup r selects row r, no workspace.
 __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(Params p) {
   __shared__ Full<kRowThreads, kRowCap> sh;
   const int r = blockIdx.x;
   const int nv = visible(p, r);
   if (nv <= p.k) select_trivial_row<kRowThreads>(p, r, nv);
-  else select_row<kRowThreads, kRowCap, kPer>(p, r, nv, sh);
+  else select_row_fit<kRowThreads, kRowCap, kPer>(p, r, nv, sh);
 }
 
 // kRowLen < max_model_len <= kWideLen: one launch, workgroup r selects row r with 32
@@ -549,7 +567,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_wide_kernel(Params p) {
   const int r = blockIdx.x;
   const int nv = visible(p, r);
   if (nv <= p.k) select_trivial_row<kRowThreads>(p, r, nv);
-  else select_row<kRowThreads, kRowCap, kWidePer>(p, r, nv, sh);
+  else select_row_fit<kRowThreads, kRowCap, kWidePer>(p, r, nv, sh);
 }
 
 // ---- Chunked mode (max_model_len > kWideLen): one launch, no schedule pass.
@@ -852,10 +870,7 @@ __global__ __launch_bounds__(kCT) void topk_chunked_kernel(Params p) {
   rewind(p, cu);
   for (uint32_t item = blockIdx.x; locate(p, cu, sh, item, it); item += gridDim.x) {
     if (it.nch != 1) continue;  // uniform
-    if (it.nv <= kRowLen)
-      select_row<kCT, kChunkCap, kPer>(p, it.r, it.nv, sh);
-    else
-      select_row<kCT, kChunkCap, kWidePer>(p, it.r, it.nv, sh);
+    select_row_fit<kCT, kChunkCap, kWidePer>(p, it.r, it.nv, sh);
   }
   for (int r = blockIdx.x; r < p.rows; r += gridDim.x) {
     const int nv = visible(p, r);
