@@ -1,7 +1,9 @@
 """mqa_topk on crafted logit rows, one call per path (every row fits one workgroup when
-max_model_len <= 8192, with 8 values per thread, or <= 32768, with 32; beyond, rows longer
-than 32768 take the chunked path inside the same launch as the whole rows), compared as
-sets with the oracle's selection (larger first, ties by lower position, -0.0 equal to +0.0).
+max_model_len <= 8192 or <= 32768, with the fewest of 4, 8, 16 or 32 values per thread
+that hold the row; beyond, rows longer than 32768 take the chunked path inside the same
+launch as the whole rows), compared as sets with the oracle's selection (larger first,
+ties by lower position, -0.0 equal to +0.0). The lengths include both sides of every
+boundary between those forms (4096, 8192, 16384, 32768).
 
 The rows are chosen to reach each branch of the selection: spread values (linear bins),
 few distinct values (a threshold bin of thousands of elements, refined by radix digits;
@@ -105,7 +107,7 @@ def run_case(L, k, specs, seed, ws=None):
 
 @pytest.mark.parametrize("k", [2048, 1, 100, 2047])
 def test_topk_rows_fit_one_workgroup(k):
-    nvs = sorted({1, 2048, 2049, 3000, 4097, 8192} | {k + 1})
+    nvs = sorted({1, 2048, 2049, 3000, 4096, 4097, 8192} | {k + 1})
     specs = [(kind, nv) for kind in KINDS for nv in nvs if nv <= 8192]
     say(f"[gpu] topk crafted rows L=8192 k={k} rows={len(specs)}")
     run_case(8192, k, specs, seed=7000 + k)
@@ -115,7 +117,7 @@ def test_topk_rows_fit_one_workgroup(k):
 def test_topk_wide_rows(k):
     """Rows up to 32768 in one workgroup each; constant, few-valued and two-valued rows
     put more than 8192 elements in the threshold bin (the refinement over the row)."""
-    nvs = [1, 2049, 8192, 8193, 20000, 32768]
+    nvs = [1, 2049, 4096, 4097, 8192, 8193, 16384, 16385, 20000, 32768]
     specs = [(kind, nv) for kind in KINDS for nv in nvs]
     say(f"[gpu] topk crafted rows L=32768 k={k} rows={len(specs)}")
     run_case(32768, k, specs, seed=7200 + k)
@@ -123,7 +125,7 @@ def test_topk_wide_rows(k):
 
 @pytest.mark.parametrize("k", [2048, 300])
 def test_topk_long_rows(k):
-    nvs = [5, 2049, 8192, 8193, 20000, 40000]
+    nvs = [5, 2049, 4096, 4097, 8192, 8193, 16384, 16385, 20000, 32768, 32769, 40000]
     specs = [(kind, nv) for kind in KINDS for nv in nvs]
     say(f"[gpu] topk crafted rows L=40000 k={k} rows={len(specs)}")
     run_case(40000, k, specs, seed=7100 + k)
