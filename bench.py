@@ -533,7 +533,8 @@ def main():
         for other in workloads.WORKLOADS:
             wo = w if other == name else workloads.make_named(other, poison_unused=False, block_size=args.block_size)
             print(f"[bench] workload {other}: sum_ctx={wo.sum_ctx}", file=sys.stderr, flush=True)
-            st_o, mo = measure(wo, args.steps, args.warmup, args.copies, other)
+            st_o, mo = measure(wo, args.steps, args.warmup, args.copies,
+                               other + (f"_bs{wo.block_size}" if wo.block_size > 1 else ""))
             table[other] = {k: v for k, v in mo.items() if k != "logits_algorithmic_bytes"}
             table[other]["block_size"] = wo.block_size
             del st_o
