@@ -144,3 +144,16 @@ def test_block_sizes(block_size, table, next_n, heads):
                         pool=nblk + 7)
     assert case.block_size == block_size
     _parity(case, what=f"S={block_size} {table} N={next_n} H={heads}")
+
+
+@pytest.mark.parametrize("block_size", [8192, 65536])
+def test_largest_block_sizes(block_size):
+    """Pages of 8192 tokens and of 65536, the largest size the call accepts: contexts that
+    end just before, at and just after a page boundary, and rows past 32768 positions
+    (the chunked top-k)."""
+    ctx = [1, 8191, 8192, 8193, 65535, 65536, 65537, 70000]
+    nblk = sum((c + block_size - 1) // block_size for c in ctx)
+    case = wl.make_case(batch=len(ctx), next_n=1, heads=64, ctx=ctx, max_model_len=70016,
+                        seed=5100 + block_size % 1000, block_size=block_size, pool=nblk + 3)
+    assert case.block_size == block_size
+    _parity(case, what=f"S={block_size}")
