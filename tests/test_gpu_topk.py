@@ -105,6 +105,15 @@ def run_case(L, k, specs, seed, ws=None):
             f"{kind} nv={nv} k={k}: {np.setdiff1d(sel, want).size} positions differ from the expected set")
 
 
+@pytest.mark.parametrize("k", [2048, 1, 100, 1023])
+def test_topk_short_rows(k):
+    """max_model_len = 4096: 4 or 8 values per thread (one 1024-thread workgroup per row)."""
+    nvs = sorted({1, 1024, 1025, 2048, 2049, 3000, 4096} | {k + 1})
+    specs = [(kind, nv) for kind in KINDS for nv in nvs if nv <= 4096]
+    say(f"[gpu] topk crafted rows L=4096 k={k} rows={len(specs)}")
+    run_case(4096, k, specs, seed=6900 + k)
+
+
 @pytest.mark.parametrize("k", [2048, 1, 100, 2047])
 def test_topk_rows_fit_one_workgroup(k):
     nvs = sorted({1, 2048, 2049, 3000, 4096, 4097, 8192} | {k + 1})
