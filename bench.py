@@ -406,20 +406,23 @@ def gather_rows(w):
 
 def gather_ceiling(st):
     """The probe's gather of the rows the logits kernel reads (same copies, same rotation),
-    best over 1, 2 and 4 workgroups of 4 waves per CU and 2 or 4 stages in flight."""
+    best over 1, 2 and 4 workgroups of 4 waves per CU and 2 or 4 stages in flight with the
+    logits kernel's register loads ("GxS"), and over 1 or 2 workgroups per CU and 2 or 3
+    stages of direct-to-LDS loads of each row's aligned 144-byte window ("lds_GxS")."""
     torch, mqa, w = st.torch, st.mqa, st.w
     rows = torch.from_numpy(gather_rows(w)).cuda()
     best, tried = None, {}
-    for gpc in (1, 2, 4):
-        for depth in (2, 4):
-            sink = torch.empty(mqa.mqa_probe_gather_sink_words(gpc), dtype=torch.int32, device="cuda")
-            fn = lambda c, gpc=gpc, sink=sink, depth=depth: mqa.mqa_probe_gather(c["kv"], rows, gpc, sink, depth)  # noqa: E731
-            us = float(np.mean(st.replay_us(st.capture(fn, st.C), st.C, 8)))
-            tried[f"{gpc}x{depth}"] = us
-            if best is None or us < best[0]:
-                best = (us, gpc, depth)
+    forms = [("", mqa.mqa_probe_gather, gpc, depth) for gpc in (1, 2, 4) for depth in (2, 4)]
+    forms += [("lds_", mqa.mqa_probe_gather_lds, gpc, depth) for gpc in (1, 2) for depth in (2, 3)]
+    for tag, probe, gpc, depth in forms:
+        sink = torch.empty(mqa.mqa_probe_gather_sink_words(gpc), dtype=torch.int32, device="cuda")
+        fn = lambda c, probe=probe, gpc=gpc, sink=sink, depth=depth: probe(c["kv"], rows, gpc, sink, depth)  # noqa: E731
+        us = float(np.mean(st.replay_us(st.capture(fn, st.C), st.C, 8)))
+        tried[f"{tag}{gpc}x{depth}"] = us
+        if best is None or us < best[0]:
+            best = (us, gpc, depth, "lds" if tag else "registers")
     n = int(rows.numel())
-    return {"us": best[0], "groups_per_cu": best[1], "stages_in_flight": best[2], "rows": n,
+    return {"us": best[0], "groups_per_cu": best[1], "stages_in_flight": best[2], "loads": best[3], "rows": n,
             "gbps_algorithmic": (ROW_BYTES + 4) * n / (best[0] * 1e-6) / 1e9,
             "us_by_groups_x_stages": tried}
 

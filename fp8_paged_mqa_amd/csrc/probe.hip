@@ -6,6 +6,10 @@
 // plus the scale dword) and folds them into one word per lane so that nothing is
 // optimised away. Its time is the ceiling a gather of those rows reaches on this GPU; the
 // paged logits kernel is measured against it.
+//
+// A second form gathers the same rows straight into LDS (global_load_lds_dwordx4): each
+// row's 16-byte-aligned 144-byte window, which holds its 132 bytes, as nine 16-byte pieces,
+// so that loads in flight cost no registers.
 #include <hip/hip_runtime.h>
 
 #include "mqa_probe.h"
@@ -74,6 +78,95 @@ __global__ __launch_bounds__(kThreads) void probe_gather_kernel(const uint8_t* k
   sink[wave * 64 + lane] = acc;
 }
 
+// Direct-to-LDS form. Per wave: DEPTH stage buffers of 64 windows (9 KB each) and the row
+// indices of a batch of kBatch stages, all in the wave's own part of LDS (no wave reads
+// another's, so no barrier). The gathers are inline asm (an LDS destination behind a
+// vector-memory counter is not something the compiler tracks), so the kernel issues its own
+// waits: a batch's row indices are loaded with ordinary loads and drained before its first
+// gather, and inside a batch the only vector-memory operations are the gathers.
+constexpr int kPieces = 9;                              // 16-byte pieces of a 144-byte window
+constexpr int kLdsStage = kStage * kPieces * 16;        // 9216 bytes: one stage of one wave
+constexpr int kBatch = 8;                               // stages whose row indices are in LDS
+constexpr int kWavesPerGroup = kThreads / 64;
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+}
+
+// 16 bytes from src into LDS bytes [m0 + 16*lane, +16).
+__device__ __forceinline__ void load_lds16(const uint8_t* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+template <int DEPTH>
+__global__ __launch_bounds__(kThreads) void probe_gather_lds_kernel(const uint8_t* kv, int64_t nrows,
+                                                                      const int32_t* rows, int64_t n,
+                                                                      int32_t* sink) {
+  static_assert(DEPTH >= 2 && DEPTH <= 3, "stages in flight");
+  __shared__ __attribute__((aligned(16))) uint8_t buf[kWavesPerGroup][DEPTH][kLdsStage];
+  __shared__ int32_t ridx[kWavesPerGroup][kBatch * kStage];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + w;
+  const int64_t nst = (n + kStage - 1) / kStage;
+  const int64_t s_lo = wave * nst / nwaves, s_hi = (wave + 1) * nst / nwaves;
+  // Last 16-byte-aligned piece start that stays inside the cache.
+  const int64_t last_piece = ((nrows * kRow) & ~(int64_t)15) - 16;
+  int acc = 0;
+  for (int64_t b0 = s_lo; b0 < s_hi; b0 += kBatch) {
+    const int nb = (int)(s_hi - b0 < kBatch ? s_hi - b0 : kBatch);
+    for (int j = 0; j < nb; ++j) {
+      const int64_t i = (b0 + j) * kStage + lane;
+      const int32_t r = rows[i < n ? i : n - 1];
+      ridx[w][j * kStage + lane] = (r < 0 || r >= nrows) ? 0 : r;  // rows outside the cache read row 0
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // indices loaded and in LDS; no gather is in flight
+    asm volatile("" ::: "memory");
+    auto issue = [&](int j, int slot) {
+      const uint32_t base = (uint32_t)(uintptr_t)&buf[w][slot][0];
+      // Addresses first (the LDS reads of the indices wait once), then the nine gathers
+      // back to back.
+      const uint8_t* src[kPieces];
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        const int ch = i * 64 + lane;  // piece ch of the stage: window ch / 9, piece ch % 9
+        const int rs = ch / kPieces, pc = ch - rs * kPieces;
+        const int64_t r = ridx[w][j * kStage + rs];
+        int64_t a = ((r * kRow) & ~(int64_t)15) + 16 * pc;
+        src[i] = kv + (a < last_piece ? a : last_piece);
+      }
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i)
+        load_lds16(src[i], (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + 1024 * i)));
+    };
+    for (int d = 0; d < DEPTH && d < nb; ++d) issue(d, d);
+    for (int j = 0; j < nb; ++j) {
+      const int after = (nb - 1 - j < DEPTH - 1) ? nb - 1 - j : DEPTH - 1;  // stages issued after j
+      if (after >= 2) wait_vm<2 * kPieces>();
+      else if (after == 1) wait_vm<kPieces>();
+      else wait_vm<0>();
+      const int slot = j % DEPTH;
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) acc ^= *reinterpret_cast<const int*>(&buf[w][slot][1024 * i + 16 * lane]);
+      wait_lgkm0();  // this slot's reads are done before it is refilled
+      if (j + DEPTH < nb) issue(j + DEPTH, slot);
+    }
+  }
+  sink[wave * 64 + lane] = acc;
+}
+
 int compute_units() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -109,6 +202,27 @@ int mqa_probe_gather(const uint8_t* kv_cache, int64_t num_rows_in_cache, const i
   else
     hipLaunchKernelGGL(probe_gather_kernel<4>, dim3(blocks), dim3(kThreads), 0, stream, kv_cache, num_rows_in_cache,
                        rows, n, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int mqa_probe_gather_lds(const uint8_t* kv_cache, int64_t num_rows_in_cache, const int32_t* rows, int64_t n,
+                         int32_t groups_per_cu, int32_t stages_in_flight, int32_t* sink, size_t sink_words,
+                         hipStream_t stream) {
+  if (n < 0 || num_rows_in_cache < 1) return 2;
+  if (groups_per_cu < 1 || groups_per_cu > 8 || (stages_in_flight != 2 && stages_in_flight != 3)) return 3;
+  if (n == 0) return 0;
+  if (!kv_cache || !rows || !sink) return 1;
+  if ((reinterpret_cast<uintptr_t>(kv_cache) & 15) != 0 || (reinterpret_cast<uintptr_t>(rows) & 3) != 0 ||
+      (reinterpret_cast<uintptr_t>(sink) & 3) != 0)
+    return 3;
+  const unsigned blocks = (unsigned)(groups_per_cu * compute_units());
+  if (sink_words < (size_t)blocks * kThreads) return 4;
+  if (stages_in_flight == 2)
+    hipLaunchKernelGGL(probe_gather_lds_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, kv_cache,
+                       num_rows_in_cache, rows, n, sink);
+  else
+    hipLaunchKernelGGL(probe_gather_lds_kernel<3>, dim3(blocks), dim3(kThreads), 0, stream, kv_cache,
+                       num_rows_in_cache, rows, n, sink);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

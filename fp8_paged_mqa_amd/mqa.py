@@ -21,7 +21,7 @@ EXPORTS = ("mqa_paged_logits", "mqa_topk", "mqa_topk_noalloc", "mqa_topk_workspa
            "mqa_indexer_k_write", "mqa_logits", "mqa_sparse_mla_decode", "mqa_sparse_mla_workspace_bytes")
 MQA_DTYPE_BF16, MQA_DTYPE_F32 = 0, 1
 # The measurement probe (include/mqa_probe.h): not part of the operation.
-PROBE_EXPORTS = ("mqa_probe_gather", "mqa_probe_gather_sink_words")
+PROBE_EXPORTS = ("mqa_probe_gather", "mqa_probe_gather_lds", "mqa_probe_gather_sink_words")
 
 
 class mqa_shape(ctypes.Structure):
@@ -73,6 +73,8 @@ def _load() -> ctypes.CDLL:
     lib.mqa_probe_gather_sink_words.restype = sz
     lib.mqa_probe_gather.argtypes = [vp, i64, vp, i64, i32, i32, vp, sz, vp]
     lib.mqa_probe_gather.restype = ctypes.c_int
+    lib.mqa_probe_gather_lds.argtypes = [vp, i64, vp, i64, i32, i32, vp, sz, vp]
+    lib.mqa_probe_gather_lds.restype = ctypes.c_int
     return lib
 
 
@@ -219,6 +221,18 @@ def mqa_probe_gather(kv_cache, rows, groups_per_cu, sink, stages_in_flight=2, st
                                _stream(stream))
     if check and st != 0:
         raise RuntimeError(f"mqa_probe_gather: status {st}")
+    return st
+
+
+def mqa_probe_gather_lds(kv_cache, rows, groups_per_cu, sink, stages_in_flight=2, stream=None,
+                         check: bool = True) -> int:
+    """The probe's direct-to-LDS form: each listed row's 16-byte-aligned 144-byte window
+    gathered into LDS (stages_in_flight 2 or 3)."""
+    st = _lib.mqa_probe_gather_lds(_ptr(kv_cache), int(kv_cache.numel() // 132), _ptr(rows), int(rows.numel()),
+                                   int(groups_per_cu), int(stages_in_flight), _ptr(sink), int(sink.numel()),
+                                   _stream(stream))
+    if check and st != 0:
+        raise RuntimeError(f"mqa_probe_gather_lds: status {st}")
     return st
 
 

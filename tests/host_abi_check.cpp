@@ -312,6 +312,15 @@ void check_other_entry_points() {
                           fake<int32_t>(0x10000), 0, nullptr),
          0, "probe nothing to read");
   expect_true(mqa_probe_gather_sink_words(2) > 0, "probe sink size");
+  expect(mqa_probe_gather_lds(fake<const uint8_t>(0x10000), 10, fake<const int32_t>(0x10000), 5, 2, 4,
+                              fake<int32_t>(0x10000), 1 << 20, nullptr),
+         3, "lds probe stages 4");
+  expect(mqa_probe_gather_lds(fake<const uint8_t>(0x10004), 10, fake<const int32_t>(0x10000), 5, 2, 3,
+                              fake<int32_t>(0x10000), 1 << 20, nullptr),
+         3, "lds probe cache not 16-byte aligned");
+  expect(mqa_probe_gather_lds(nullptr, 10, fake<const int32_t>(0x10000), 0, 2, 2, fake<int32_t>(0x10000), 0,
+                              nullptr),
+         0, "lds probe nothing to read");
   // status strings
   for (int st = -1; st <= 8; ++st) expect_true(mqa_status_string(st) != nullptr, "status string");
   expect_true(std::strcmp(mqa_status_string(MQA_OK), "ok") == 0, "status string of MQA_OK");

@@ -53,6 +53,13 @@ def test_probe_host_checks():
     assert probe(None, 10, FAKE, 5, 2, 2, sink, 1 << 20, None) == 1
     assert probe(ctypes.c_void_p(0x10002), 10, FAKE, 5, 2, 2, sink, 1 << 20, None) == 3
     assert probe(FAKE, 10, FAKE, 0, 2, 2, sink, 0, None) == 0
+    lds = mqa._lib.mqa_probe_gather_lds
+    assert lds(FAKE, 10, FAKE, -1, 2, 2, sink, 1 << 20, None) == 2
+    assert lds(FAKE, 10, FAKE, 5, 2, 4, sink, 1 << 20, None) == 3    # 2 or 3 stages
+    assert lds(FAKE, 10, FAKE, 5, 9, 2, sink, 1 << 20, None) == 3
+    assert lds(None, 10, FAKE, 5, 2, 3, sink, 1 << 20, None) == 1
+    assert lds(ctypes.c_void_p(0x10004), 10, FAKE, 5, 2, 3, sink, 1 << 20, None) == 3  # cache 16-byte aligned
+    assert lds(FAKE, 10, FAKE, 0, 2, 3, sink, 0, None) == 0
 
 
 def test_status_strings():
