@@ -196,7 +196,7 @@ __device__ __forceinline__ int locate(const int* a, int n, int x) {
 
 // Up to 4 row tiles fit two waves per SIMD (<= 256 VGPRs); the 5..8-tile variants (H > 64,
 // or several decode rows per wave with pages under 64 tokens) take the whole register file.
-template <int TPJ, int JPG>
+template <int TPJ, int JPG, bool SMALL>
 __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logits_kernel(Params p) {
   constexpr int TILES = TPJ * JPG;  // MFMA row tiles (16 heads each) held by one wave
   static_assert(TILES >= 1 && TILES <= 8, "query tile budget");
@@ -217,25 +217,60 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   const int g = lane >> 4;   // lane group: k-slice for operands, row quad for results
   const int c = lane & 15;   // column (token) / row (head) within a 16-wide tile
   const int L = p.L;
+  const int nwaves = gridDim.x * kWavesPerGroup;
+  const int gw = blockIdx.x * kWavesPerGroup + wave;
+
+  // Small calls (one row group, at most 64 requests, and a wave for every stage of every
+  // request at its largest context): wave gw owns stage gw / B of request gw % B. Its table
+  // entries and query rows are loaded at once, beside the context lengths, so no schedule
+  // stands between the start and the first gathers.
+  const int sb = SMALL ? gw % B : 0;
+  const int ss = SMALL ? gw / B : 0;
+  int tab_s = 0;
+  i32x4 qraw_s[SMALL ? TILES : 1][2];
+  f32x4 wv_s[SMALL ? TILES : 1];
+  if constexpr (SMALL) {
+    tab_s = p.bt[(int64_t)sb * p.W + min((ss * kStage + lane) >> p.bshift, p.W - 1)];
+    const int jn_s = min(JPG, p.N);
+    const uint8_t* qb = p.q + (int64_t)sb * p.N * p.H * kD;
+    const float* wb = p.w + (int64_t)sb * p.N * p.H;
+#pragma unroll
+    for (int m = 0; m < TILES; ++m) {
+      const int mr = min(m / TPJ, jn_s - 1) * TPJ + m % TPJ;
+      const uint8_t* qr = qb + (mr * 16 + c) * kD;
+      qraw_s[m][0] = load16(qr + 16 * g);
+      qraw_s[m][1] = load16(qr + 64 + 16 * g);
+      wv_s[m] = *reinterpret_cast<const f32x4*>(wb + mr * 16 + 4 * g);
+    }
+  }
 
   // ---- Schedule: per request, the number of 64-token key stages and of tail chunks.
   // Up to 64 requests they stay in registers, lane b holding request b (read back with
   // readlane at a wave-uniform index); beyond, in LDS.
   int r_ctx = 0, r_pref = 0, r_tail = 0, tot_pref = 0, tot_tail = 0;
+  int v_all = 0, v_below = 0;  // small calls: stages that exist, and those of the waves below gw
   if (per_wave) {
-    int nu = 0, nc = 0;
+    int nu = 0, nc = 0, va = 0, vb = 0;
     if (lane < B) {
       r_ctx = max(0, min(p.ctx_lens[lane], min(p.Wt, L)));
       const int ns = (r_ctx + kStage - 1) / kStage;
       const int tail0 = ns * kStage;
       nc = tail0 < L ? p.N * ((L - tail0 + kTailChunk - 1) / kTailChunk) : 0;
       nu = ns > 0 ? ns + kStartUnits : 0;
+      if (SMALL) {  // request `lane`'s stages belong to waves lane, lane + B, ...
+        va = ns;
+        vb = min(ns, gw > lane ? (gw - 1 - lane) / B + 1 : 0);
+      }
     }
     const int iu = (int)wave_scan_add((uint32_t)nu), ic = (int)wave_scan_add((uint32_t)nc);
     r_pref = iu - nu;
     r_tail = ic - nc;
     tot_pref = __builtin_amdgcn_readlane(iu, kWave - 1);  // lanes past B add nothing
     tot_tail = __builtin_amdgcn_readlane(ic, kWave - 1);
+    if (SMALL) {
+      v_all = __builtin_amdgcn_readlane((int)wave_scan_add((uint32_t)va), kWave - 1);
+      v_below = __builtin_amdgcn_readlane((int)wave_scan_add((uint32_t)vb), kWave - 1);
+    }
   } else {
     const int per = (B + kThreads - 1) / kThreads;  // requests per thread, consecutive
     const int r0 = threadIdx.x * per;
@@ -285,9 +320,6 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
     return per_wave ? (i >= B ? tot_tail : __builtin_amdgcn_readlane(r_tail, i)) : tail_pref[i];
   };
 
-  const int nwaves = gridDim.x * kWavesPerGroup;
-  const int gw = blockIdx.x * kWavesPerGroup + wave;
-
   // ---- Key stages.
   const int G = p.groups;
   const int group = gw % G;
@@ -298,9 +330,101 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   // Share [floor(wi*S/nw), floor((wi+1)*S/nw)) in 32-bit arithmetic: with S = sq*nw + sr,
   // floor(wi*S/nw) = wi*sq + floor(wi*sr/nw), and wi*sr < nw^2 fits. sr waves of each
   // group take sq + 1 units, the others sq.
-  const int S = pref_at(B);
+  const int S = SMALL ? 0 : pref_at(B);
   const int sq = S / nw, sr = S - sq * nw;
-  if (wi < nw) {
+  const bool s_valid = SMALL && ss < (ctx_at(sb) + kStage - 1) / kStage;  // this wave's small-call stage exists
+  const uint8_t* kv_g = p.kv + 16 * g;  // this lane's first key slice
+  const uint8_t* kv_s = p.kv + kD;      // scales
+  {
+    // One 64-token stage starting at token tok0 of the request whose table entries (lane l:
+    // the entry of token tok0 + l) are in tab: its rows' keys into the B-operand slots of s
+    // (row 0 when the stage is not live or an entry is outside the cache).
+    auto gather_stage = [&](int tok0, bool live, int tab, Stage& s) {
+      int ph[kTilesPerStage];
+#pragma unroll
+      for (int u = 0; u < kTilesPerStage; ++u) ph[u] = __shfl(tab, u * 16 + c);
+      const uint32_t smask = (1u << p.bshift) - 1u;  // slot of a token in its block
+      const uint32_t tok = (uint32_t)(tok0 + c);
+#pragma unroll
+      for (int u = 0; u < kTilesPerStage; ++u) {
+        const uint32_t slot = (tok + 16u * u) & smask;
+        const uint32_t row = (live && (uint32_t)ph[u] < p.nblk) ? ((uint32_t)ph[u] << p.bshift) | slot : 0u;
+        const uint8_t* kp = kv_g + (uint64_t)row * kRow;
+        s.phys[u] = ph[u];
+        s.lo[u] = load16(kp);
+        s.hi[u] = load16(kp + 64);
+        s.scale[u] = *reinterpret_cast<const float*>(kv_s + (uint64_t)row * kRow);
+      }
+    };
+    // The stage at token tc: contraction, epilogue and the stores of its 64 logits for the
+    // jn owned decode rows (row jl of out0 + jl * L; positions from t_need on are past ctx,
+    // from nv[jl] on past the row's causal limit, from t_end on past the output row).
+    auto compute_stage = [&](const Operand (&qa)[TILES], const f32x4 (&wv)[TILES], const Stage& s, int tc,
+                             int t_need, int t_end, const int (&nv)[JPG], float* out0, int jn) {
+      float keep[JPG];
+#pragma unroll
+      for (int jl = 0; jl < JPG; ++jl) keep[jl] = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kTilesPerStage; ++u) {
+        const int t = tc + u * 16 + c;
+        const bool in_ctx = t < t_need;
+        const bool ok = in_ctx && (uint32_t)s.phys[u] < p.nblk;
+        // Past ctx the column is masked below; a bad table entry poisons it with NaN.
+        const float sc = ok ? s.scale[u] : (in_ctx ? __builtin_nanf("") : 0.0f);
+        i32x4 lo = s.lo[u], hi = s.hi[u];
+        if (__ballot(__float_as_int(sc) < 0) != 0) {  // wave-uniform: rare
+          const int flip = (__float_as_int(sc) < 0) ? (int)0x80808080 : 0;
+          lo ^= flip;
+          hi ^= flip;
+        }
+        const Operand kb = to_operand(lo, hi);
+        const float sabs = __builtin_fabsf(sc);
+        f32x4 acc[TILES];
+#pragma unroll
+        for (int m = 0; m < TILES; ++m) {
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[0], kb.k[0], f32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+          for (int k = 1; k < 4; ++k)
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[k], kb.k[k], acc[m], 0, 0, 0);
+        }
+#pragma unroll
+        for (int jl = 0; jl < JPG; ++jl) {
+          float part = 0.0f;
+#pragma unroll
+          for (int mm = 0; mm < TPJ; ++mm) {
+            const int m = jl * TPJ + mm;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              part = __builtin_fmaf(wv[m][v], __builtin_elementwise_maximum(acc[m][v], 0.0f), part);
+          }
+          part = sum_lane_groups(part);
+          if (g == u) keep[jl] = part * sabs;
+        }
+      }
+      const int t = tc + lane;  // lane (g, c) stores token 16g + c of the stage
+      if (t < t_end) {
+#pragma unroll
+        for (int jl = 0; jl < JPG; ++jl)
+          if (jl < jn) out0[(int64_t)jl * L + t] = (t < nv[jl]) ? keep[jl] : -__builtin_inff();
+      }
+    };
+    if constexpr (SMALL) {
+      if (s_valid) {  // wave-uniform
+        const int ctx = ctx_at(sb);
+        const int tc = ss * kStage;
+        const int t_end = min(tc + kStage, L);
+        const int t_need = min(t_end, ctx);
+        int nv[JPG];
+#pragma unroll
+        for (int jl = 0; jl < JPG; ++jl) nv[jl] = min(ctx - p.N + jl + 1, L);
+        Stage sx;
+        gather_stage(tc, true, tab_s, sx);
+        Operand qs[TILES];
+#pragma unroll
+        for (int m = 0; m < TILES; ++m) qs[m] = to_operand(qraw_s[m][0], qraw_s[m][1]);
+        compute_stage(qs, wv_s, sx, tc, t_need, t_end, nv, p.out + (int64_t)sb * p.N * L, min(JPG, p.N));
+      }
+    } else if (wi < nw) {
     int lo = wi * sq + (wi * sr) / nw;
     const int hi = (wi + 1) * sq + ((wi + 1) * sr) / nw;
     int b = 0;
@@ -312,8 +436,6 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         b = locate(stage_pref, B, lo);
       }
     }
-    const uint8_t* kv_g = p.kv + 16 * g;  // this lane's first key slice
-    const uint8_t* kv_s = p.kv + kD;      // scales
     while (lo < hi) {
       // Segment: stages [s0, s0 + nstage) of request b, the stages whose units fall in
       // [lo, seg_hi); none when the share holds only the request's start units.
@@ -362,73 +484,10 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         __builtin_amdgcn_sched_barrier(0);
         Operand qa[TILES];
 
-        auto issue_keys = [&](int st, int tab, Stage& s) {
-          const bool live = st < nstage;  // wave-uniform
-          int ph[kTilesPerStage];
-#pragma unroll
-          for (int u = 0; u < kTilesPerStage; ++u) ph[u] = __shfl(tab, u * 16 + c);
-          const uint32_t smask = (1u << p.bshift) - 1u;  // slot of a token in its block
-          const uint32_t tok = (uint32_t)(t0 + st * kStage + c);
-#pragma unroll
-          for (int u = 0; u < kTilesPerStage; ++u) {
-            const uint32_t slot = (tok + 16u * u) & smask;
-            const uint32_t row = (live && (uint32_t)ph[u] < p.nblk) ? ((uint32_t)ph[u] << p.bshift) | slot : 0u;
-            const uint8_t* kp = kv_g + (uint64_t)row * kRow;
-            s.phys[u] = ph[u];
-            s.lo[u] = load16(kp);
-            s.hi[u] = load16(kp + 64);
-            s.scale[u] = *reinterpret_cast<const float*>(kv_s + (uint64_t)row * kRow);
-          }
-        };
+        auto issue_keys = [&](int st, int tab, Stage& s) { gather_stage(t0 + st * kStage, st < nstage, tab, s); };
 
         auto compute_store = [&](int st, const Stage& s) {
-          const int tc = t0 + st * kStage;
-          float keep[JPG];
-#pragma unroll
-          for (int jl = 0; jl < JPG; ++jl) keep[jl] = 0.0f;
-#pragma unroll
-          for (int u = 0; u < kTilesPerStage; ++u) {
-            const int t = tc + u * 16 + c;
-            const bool in_ctx = t < t_need;
-            const bool ok = in_ctx && (uint32_t)s.phys[u] < p.nblk;
-            // Past ctx the column is masked below; a bad table entry poisons it with NaN.
-            const float sc = ok ? s.scale[u] : (in_ctx ? __builtin_nanf("") : 0.0f);
-            i32x4 lo = s.lo[u], hi = s.hi[u];
-            if (__ballot(__float_as_int(sc) < 0) != 0) {  // wave-uniform: rare
-              const int flip = (__float_as_int(sc) < 0) ? (int)0x80808080 : 0;
-              lo ^= flip;
-              hi ^= flip;
-            }
-            const Operand kb = to_operand(lo, hi);
-            const float sabs = __builtin_fabsf(sc);
-            f32x4 acc[TILES];
-#pragma unroll
-            for (int m = 0; m < TILES; ++m) {
-              acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[0], kb.k[0], f32x4{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-              for (int k = 1; k < 4; ++k)
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[k], kb.k[k], acc[m], 0, 0, 0);
-            }
-#pragma unroll
-            for (int jl = 0; jl < JPG; ++jl) {
-              float part = 0.0f;
-#pragma unroll
-              for (int mm = 0; mm < TPJ; ++mm) {
-                const int m = jl * TPJ + mm;
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                  part = __builtin_fmaf(wv[m][v], __builtin_elementwise_maximum(acc[m][v], 0.0f), part);
-              }
-              part = sum_lane_groups(part);
-              if (g == u) keep[jl] = part * sabs;
-            }
-          }
-          const int t = tc + lane;  // lane (g, c) stores token 16g + c of the stage
-          if (t < t_end) {
-#pragma unroll
-            for (int jl = 0; jl < JPG; ++jl)
-              if (jl < jn) out0[(int64_t)jl * L + t] = (t < nv[jl]) ? keep[jl] : -__builtin_inff();
-          }
+          compute_stage(qa, wv, s, t0 + st * kStage, t_need, t_end, nv, out0, jn);
         };
 
         // Software pipeline: keys of two stages in flight, table entries two stages ahead
@@ -461,19 +520,21 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
       ++b;
       while (b < B && pref_at(b + 1) <= lo) ++b;  // skip requests without stages
     }
+    }
   }
 
   // ---- -inf tail: positions past each request's last key stage, every row. Each wave
   // takes a contiguous run of 1 KB chunks and walks it row by row (LDS is read only
   // where the run enters another request).
   {
-    // The waves with a longer stage share (sq + 1 units) take kStageChunks chunks fewer
-    // than the others (none if the tail is short), so they are not the last to finish:
-    // heavy waves split the first C_H chunks equally, the light ones the rest.
+    // The waves with a longer stage share (sq + 1 units; in a small call, the waves that
+    // own a stage) take kStageChunks chunks fewer than the others (none if the tail is
+    // short), so they are not the last to finish: heavy waves split the first C_H chunks
+    // equally, the light ones the rest.
     const int C = tail_at(B);
-    const bool heavy = wi < nw && ((wi + 1) * sr) / nw > (wi * sr) / nw;
-    const int heavy_before = G * min((wi * sr) / nw, sr) + (heavy ? group : 0);
-    const int nH = G * sr, nL = nwaves - nH;
+    const int nH = SMALL ? (v_all < nwaves ? v_all : 0) : G * sr, nL = nwaves - nH;
+    const bool heavy = SMALL ? (s_valid && nH > 0) : (wi < nw && ((wi + 1) * sr) / nw > (wi * sr) / nw);
+    const int heavy_before = SMALL ? (nH > 0 ? v_below : 0) : G * min((wi * sr) / nw, sr) + (heavy ? group : 0);
     const int cH = max(0, (int)(((uint32_t)C + (uint32_t)nH * kStageChunks) / (uint32_t)nwaves) - kStageChunks);
     const int CH = nH * cH, CL = C - CH;
     int ci, ce;
@@ -528,7 +589,9 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
 using KernelFn = void (*)(Params);
 
 template <int TPJ, int JPG>
-constexpr KernelFn kfn() { return paged_logits_kernel<TPJ, JPG>; }
+constexpr KernelFn kfn() { return paged_logits_kernel<TPJ, JPG, false>; }
+template <int TPJ, int JPG>
+constexpr KernelFn kfs() { return paged_logits_kernel<TPJ, JPG, true>; }
 
 // [TPJ-1][JPG-1]; TPJ = H/16 in 1..8, JPG = decode rows per wave: min(N, T/TPJ) with
 // T = 8 row tiles (128 f16 query VGPRs) for pages under 64 tokens and T = 4 (64 VGPRs,
@@ -542,6 +605,14 @@ constexpr KernelFn kTable[8][4] = {
     {kfn<6, 1>(), nullptr, nullptr, nullptr},
     {kfn<7, 1>(), nullptr, nullptr, nullptr},
     {kfn<8, 1>(), nullptr, nullptr, nullptr},
+};
+
+// Small-call forms, [TPJ-1][JPG-1] for up to 4 row tiles.
+constexpr KernelFn kTableSmall[4][4] = {
+    {kfs<1, 1>(), kfs<1, 2>(), kfs<1, 3>(), kfs<1, 4>()},
+    {kfs<2, 1>(), kfs<2, 2>(), nullptr, nullptr},
+    {kfs<3, 1>(), nullptr, nullptr, nullptr},
+    {kfs<4, 1>(), nullptr, nullptr, nullptr},
 };
 
 // Compute units of the current device, read once per device.
@@ -610,6 +681,11 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   const int64_t per_cu = (a.block_shift >= 6 && p.groups > 1 && tpj * jpg <= 4) ? 2 : 1;
   const int64_t full = per_cu * compute_units();
   const int blocks = (int)std::max<int64_t>(1, std::min(full, need));
+  // Small calls: when that grid holds a wave for every stage of every request at its largest
+  // context (one row group, at most 64 requests), each wave takes one stage, fixed by its
+  // index, and issues its table and query loads beside the context lengths: the schedule's
+  // round trips (context lengths, then table entries, then keys) become one.
+  if (a.batch <= kWave && p.groups == 1 && tpj * jpg <= 4 && need <= full) fn = kTableSmall[tpj - 1][jpg - 1];
   hipLaunchKernelGGL(fn, dim3(blocks), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }

@@ -43,6 +43,20 @@ def test_batch_composition_and_length_bitwise():
         assert np.all(g[:, 12000:] == -np.inf)
 
 
+def test_small_call_rows_match_large_call_bitwise():
+    """A request alone in a small call (each wave's stage fixed by its index) gives the same
+    bits as inside a batch large enough for the scheduled form."""
+    ctx = [1, 63, 64, 65, 2049, 4096, 700, 3000] * 5
+    case = wl.make_case(batch=len(ctx), next_n=1, heads=64, ctx=ctx, max_model_len=8192, seed=54)
+    full, _ = run_gpu(case)
+    for b in [0, 2, 3, 4, 5]:
+        alone = wl.Workload("alone", case.q[b:b + 1], case.kv_cache, case.weights[b:b + 1],
+                            case.context_lens[b:b + 1], case.block_tables[b:b + 1], 4096, 1)
+        g, _ = run_gpu(alone)
+        assert np.array_equal(g[0].view(np.uint32), full[b, :4096].view(np.uint32)), b
+        assert np.all(full[b, 4096:] == -np.inf)
+
+
 def test_repeatable():
     case = wl.make_named("mtp_b32_n2_ctx32k")
     g1, i1 = run_gpu(case)

@@ -123,6 +123,32 @@ def test_request_counts(batch, max_ctx):
     _parity(case, what=f"B={batch}")
 
 
+# Small calls (at most 64 requests, one row group, and a grid of no more than one workgroup
+# per CU holding a wave for every stage of every request at its largest context) take the
+# form where each wave's stage is fixed by its index. Shapes on both sides of the size limit
+# (64 requests, H = 16, L = 960 fits exactly; L = 1024 does not), empty and full contexts,
+# a context filling every stage with no tail, several decode rows per wave, 16-token pages.
+@pytest.mark.parametrize("batch,next_n,heads,L,ctx,block_size", [
+    (64, 1, 16, 960, "random", 1),
+    (64, 1, 16, 1024, "random", 1),
+    (1, 1, 64, 192, [192], 1),
+    (3, 1, 64, 4096, [0, 64, 4096], 1),
+    (4, 4, 16, 2048, [1, 100, 2048, 1000], 1),
+    (16, 2, 32, 2048, "random", 1),
+    (5, 1, 32, 2048, [17, 2048, 1, 640, 1999], 16),
+])
+def test_small_calls(batch, next_n, heads, L, ctx, block_size):
+    if ctx == "random":
+        rng = np.random.default_rng(7000 + batch + L)
+        ctx = rng.integers(0, L + 1, batch)
+        ctx[0], ctx[-1] = L, 0
+        ctx = ctx.tolist()
+    nblk = sum((c + block_size - 1) // block_size for c in ctx)
+    case = wl.make_case(batch=batch, next_n=next_n, heads=heads, ctx=ctx, max_model_len=L,
+                        seed=7100 + batch + L, block_size=block_size, pool=nblk + 5)
+    _parity(case, what=f"small B={batch} N={next_n} H={heads} L={L} S={block_size}")
+
+
 @pytest.mark.parametrize("k", [1, 7, 100, 2047, 2048])
 def test_k_values(k):
     case = wl.make_case(batch=6, next_n=2, heads=32, ctx=[1, 2, 100, 2048, 2050, 9000],
