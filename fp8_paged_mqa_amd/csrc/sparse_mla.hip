@@ -79,14 +79,16 @@ struct Params {
   const int32_t* bt;     // [B, W]
   float* out;            // [R, 16, 512]
   float* lse;            // [R, 16] or null
-  float* ws;             // [R, splits, kPartial] (splits > 1)
+  uint8_t* ws;           // [R, splits] partial states of kPartialBytes (splits > 1)
   float c2;              // sm_scale * q_scale * kv_scale * log2(e)
   float vscale;          // kv_scale (O and l both carry the 2^15 of the probabilities)
   int32_t R, N, topk, W, bshift, splits, tps;
   uint32_t nblk;         // blocks in the cache (clamped to 2^31 - 1)
 };
 
-constexpr int kPartial = kH * kDV + 2 * kH;  // O, then m, then l, per split
+// Partial state of a split: O / l per head and column as f16 (the weighted mean of value
+// codes, |O / l| <= 448, so f16 holds it to 2^-11), then m and l per head as f32.
+constexpr int kPartialBytes = kH * kDV * 2 + 2 * kH * 4;
 
 struct Smem {
   uint8_t tile[kNBuf][kTileBytes];
@@ -373,41 +375,50 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
       p.lse[(int64_t)r * kH + i] =
           l_run > 0.0f ? (m_run + __builtin_amdgcn_logf(l_run) - 15.0f) * kLn2 : (l_run == 0.0f ? -__builtin_inff() : l_run);
   } else {
-    float* part = p.ws + ((int64_t)r * p.splits + split) * kPartial;
-    float* orow = part + i * kDV + 128 * wave + 4 * G;
+    uint8_t* part = p.ws + ((int64_t)r * p.splits + split) * kPartialBytes;
+    _Float16* orow = reinterpret_cast<_Float16*>(part) + i * kDV + 128 * wave + 4 * G;
+    // A split that saw nothing stores 0 (its weight in the merge is 0); NaN stays NaN.
+    const float inv = l_run > 0.0f ? 1.0f / l_run : (l_run == 0.0f ? 0.0f : l_run);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) *reinterpret_cast<f32x4*>(orow + 16 * ct) = o[ct];
+    for (int ct = 0; ct < 8; ++ct) {
+      const f32x4 v = o[ct] * inv;
+      *reinterpret_cast<f16x4*>(orow + 16 * ct) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    }
     if (wave == 0 && G == 0) {
-      part[kH * kDV + i] = m_run;
-      part[kH * kDV + kH + i] = l_run;
+      float* ml = reinterpret_cast<float*>(part + kH * kDV * 2);
+      ml[i] = m_run;
+      ml[kH + i] = l_run;
     }
   }
 }
 
-// Merges the splits' partial states (grid (16 heads, rows), 128 threads, a float4 of
-// columns per thread) in one pass with a running maximum: per split, M' = max(M, m_s),
-// acc = acc * 2^(M - M') + 2^(m_s - M') * O_s, L likewise; out = kv_scale * acc / L.
+// Merges the splits' partial states (grid (16 heads, rows), 128 threads, four columns per
+// thread) in one pass with a running maximum: per split, M' = max(M, m_s),
+// acc = acc * 2^(M - M') + 2^(m_s - M') * l_s * (O_s / l_s), L = L * 2^(M - M') + 2^(m_s - M') * l_s;
+// out = kv_scale * acc / L.
 // The loads of consecutive splits do not depend on each other, so they are in flight
 // together.
 __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(Params p) {
   const int h = blockIdx.x;
   const int r = blockIdx.y;
-  const float* base = p.ws + (int64_t)r * p.splits * kPartial;
+  const uint8_t* base = p.ws + (int64_t)r * p.splits * kPartialBytes;
   float M = -__builtin_inff();
   float L = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 8
   for (int s = 0; s < p.splits; ++s) {
-    const float* part = base + s * kPartial;
-    const float ms = part[kH * kDV + h];
-    const float ls = part[kH * kDV + kH + h];
-    const f32x4 os = *reinterpret_cast<const f32x4*>(part + h * kDV + 4 * threadIdx.x);
+    const uint8_t* part = base + s * kPartialBytes;
+    const float* ml = reinterpret_cast<const float*>(part + kH * kDV * 2);
+    const float ms = ml[h];
+    const float ls = ml[kH + h];
+    const f16x4 oh = *reinterpret_cast<const f16x4*>(part + (h * kDV + 4 * threadIdx.x) * 2);
+    const f32x4 os = {(float)oh[0], (float)oh[1], (float)oh[2], (float)oh[3]};  // O_s / l_s
     const float mn = __builtin_fmaxf(M, ms);
     const float mu = mn == -__builtin_inff() ? 0.0f : mn;
     const float a = __builtin_amdgcn_exp2f(M - mu);   // 0 while nothing has been seen
-    const float w = __builtin_amdgcn_exp2f(ms - mu);  // 0 for a split that saw nothing
+    const float w = __builtin_amdgcn_exp2f(ms - mu) * ls;  // 0 for a split that saw nothing
     acc = acc * a + os * w;
-    L = L * a + ls * w;
+    L = L * a + w;
     M = mn;
   }
   const float f = L == 0.0f ? 0.0f : p.vscale / L;
@@ -433,7 +444,7 @@ SparseMlaPlan sparse_mla_plan(int64_t rows, int32_t topk) {
   tps = tps < 1 ? 1 : (tps > kMaxTiles ? kMaxTiles : tps);
   plan.tiles_per_split = (int32_t)tps;
   plan.splits = (int32_t)((tiles + tps - 1) / tps);
-  plan.workspace_bytes = plan.splits > 1 ? (size_t)rows * plan.splits * kPartial * sizeof(float) : 0;
+  plan.workspace_bytes = plan.splits > 1 ? (size_t)rows * plan.splits * kPartialBytes : 0;
   return plan;
 }
 
@@ -446,7 +457,7 @@ hipError_t launch_sparse_mla(const SparseMlaLaunch& a, const SparseMlaPlan& plan
   p.bt = a.bt;
   p.out = a.out;
   p.lse = a.lse;
-  p.ws = reinterpret_cast<float*>(a.workspace);
+  p.ws = static_cast<uint8_t*>(a.workspace);
   p.c2 = a.sm_scale * a.q_scale * a.kv_scale * 1.4426950408889634f;
   p.vscale = a.kv_scale;
   p.R = (int32_t)a.rows;

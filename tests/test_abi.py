@@ -317,7 +317,7 @@ def test_sparse_mla_zero_rows_is_a_no_op():
 def test_sparse_mla_workspace():
     big = mla_shape(batch=64, next_n=1, topk=2048)
     need = mqa.mqa_sparse_mla_workspace_bytes(big)
-    assert need > 0 and need % (4 * (16 * 512 + 32)) == 0
+    assert need > 0 and need % (2 * 16 * 512 + 4 * 2 * 16) == 0  # per split: f16 mean, f32 max and sum
     assert call_mla(big) == mqa.MQA_ERR_WORKSPACE
     assert call_mla(big, ws=FAKE, ws_bytes=need - 1) == mqa.MQA_ERR_WORKSPACE
     assert mqa.mqa_sparse_mla_workspace_bytes(mla_shape(batch=1, next_n=1, topk=64)) == 0

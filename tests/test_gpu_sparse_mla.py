@@ -3,8 +3,10 @@
 Tolerance, from the arithmetic of the kernel: the scores' dot products are exact
 products summed in fp32 (576 terms), the probabilities are rounded to f16 (relative
 2^-11) before the value contraction, and the weights of the convex combination are
-normalised by the sum of those rounded values. Per output element that bounds the
-error by a few 2^-11 of B = kv_scale * sum_t p_t |v_t| (the oracle computes B), so:
+normalised by the sum of those rounded values; a split's partial output is kept as its
+weighted mean of value codes in f16 (relative 2^-11 again) until the merge. Per output
+element that bounds the error by a few 2^-11 of B = kv_scale * sum_t p_t |v_t| (the oracle
+computes B), so:
     |gpu - oracle| <= 4e-3 * B + 1e-6 * kv_scale
 and for the log-sum-exp |gpu - oracle| <= 2e-3 + 1e-6 * |oracle|. The pages judge MLA
 decode by the cosine difference of the whole output against a reference (about 5e-4
