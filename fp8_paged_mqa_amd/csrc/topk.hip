@@ -617,10 +617,19 @@ enum { kCntHist = 0, kCntSplit = 1, kCntEmit = 2, kCntCand = 3 };
 // (~0.5 us each, with a short sleep between polls).
 constexpr int kWaitPolls = 1 << 16;
 
-// Items of a row with nv visible positions: 0 when the row is trivial, 1 when it is
-// selected whole, else its chunk count (at least 5).
+// Chunk items of a row with nv visible positions: its chunk count (at least 5) when it is
+// longer than a workgroup selects whole, else 0.
 __device__ __forceinline__ uint32_t chunks_of(const Params& p, int nv) {
-  return nv <= p.k ? 0u : nv <= kWideLen ? 1u : (uint32_t)((nv + kChunk - 1) / kChunk);
+  return nv > kWideLen ? (uint32_t)((nv + kChunk - 1) / kChunk) : 0u;
+}
+
+// Rows selected whole (k < nv <= kWideLen) fall in four cost classes, heaviest first: the
+// values per thread select_row_fit gives them (32, 16, 8, 4), each costing about twice the
+// next. -1 for every other row.
+constexpr int kWholeClasses = 4;
+__device__ __forceinline__ int whole_class(const Params& p, int nv) {
+  if (nv <= p.k || nv > kWideLen) return -1;
+  return nv > 16 * kCT ? 0 : nv > 8 * kCT ? 1 : nv > 4 * kCT ? 2 : 3;
 }
 
 // Walks the chunk items of a call in increasing order, rows kCT at a time: thread t holds
@@ -648,9 +657,11 @@ __device__ __forceinline__ void rewind(const Params& p, Cursor& cu) {
   }
 }
 
-// Finds chunk item `item`; returns false past the last one. Every thread calls it with the
-// same item, and the items of successive calls (after a rewind) do not decrease.
-__device__ bool locate(const Params& p, Cursor& cu, Core<kCT>& sh, uint32_t item, Item& it) {
+// Finds item `item` of the numbering in which row r holds count(nv_r) consecutive items;
+// returns false past the last one. Every thread calls it with the same item, and the
+// items of successive calls (after a rewind) do not decrease.
+template <typename Count>
+__device__ bool locate(const Params& p, Cursor& cu, Core<kCT>& sh, uint32_t item, Item& it, Count count) {
   __syncthreads();  // the previous item's readers of sh.loc and of the scan scratch are done
   while (item >= cu.first + cu.total) {  // uniform
     cu.first += cu.total;
@@ -658,7 +669,7 @@ __device__ bool locate(const Params& p, Cursor& cu, Core<kCT>& sh, uint32_t item
     if (cu.base >= p.rows) return false;
     const int row = cu.base + (int)threadIdx.x;
     cu.nv = row < p.rows ? visible(p, row) : 0;
-    cu.nch = chunks_of(p, cu.nv);
+    cu.nch = count(cu.nv);
     cu.excl = block_exclusive_scan<kCT>(cu.nch, sh, kRedLoc, cu.total);
     __syncthreads();  // every thread has read the scan scratch
   }
@@ -842,14 +853,70 @@ __device__ void split_chunk(const Params& p, ChunkFull& sh, const Item& it, cons
   if (sh.last) finish_row(p, sh, it, bin0, above, cnt0);  // uniform
 }
 
+// Items of the call: chunk items, then the whole rows of each cost class (one reduction
+// pass over the rows, one barrier per block of rows; the per-class counts of one block
+// fit 16 bits). When every row is in one block that the chunk cursor has scanned, the
+// visible counts are the cursor's and nothing is loaded.
+struct ItemTotals {
+  uint32_t chunks;
+  uint32_t whole[kWholeClasses];
+};
+__device__ ItemTotals item_totals(const Params& p, Core<kCT>& sh, const Cursor& cu) {
+  constexpr int W = kCT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const bool cached = p.rows <= kCT && cu.base == 0;  // uniform
+  ItemTotals t = {0u, {0u, 0u, 0u, 0u}};
+  for (int base = 0; base < p.rows; base += kCT) {
+    const int row = base + (int)threadIdx.x;
+    const int nv = cached ? cu.nv : (row < p.rows ? visible(p, row) : 0);
+    const int cls = whole_class(p, nv);
+    const uint32_t a = wave_scan_add(chunks_of(p, nv));
+    const uint32_t b = wave_scan_add((cls == 0 ? 1u : 0u) | (cls == 1 ? 1u << 16 : 0u));
+    const uint32_t c = wave_scan_add((cls == 2 ? 1u : 0u) | (cls == 3 ? 1u << 16 : 0u));
+    if (base > 0) __syncthreads();  // the previous block's readers of these slots are done
+    if (lane == 63) {
+      sh.red[kRedLo * W + wave] = a;
+      sh.red[kRedHi * W + wave] = b;
+      sh.red[kRedBad * W + wave] = c;
+    }
+    __syncthreads();
+    uint32_t ta = 0, tb = 0, tc = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      ta += sh.red[kRedLo * W + w];
+      tb += sh.red[kRedHi * W + w];
+      tc += sh.red[kRedBad * W + w];
+    }
+    t.chunks += ta;
+    t.whole[0] += tb & 0xFFFFu;
+    t.whole[1] += tb >> 16;
+    t.whole[2] += tc & 0xFFFFu;
+    t.whole[3] += tc >> 16;
+  }
+  // No barrier here: the next writers of these scratch slots (a row select) run after
+  // locate()'s barrier.
+  return t;
+}
+
 __global__ __launch_bounds__(kCT) void topk_chunked_kernel(Params p) {
   __shared__ ChunkFull sh;
   const int tid = (int)threadIdx.x;
+  // Work is dealt out in one list, heaviest items first: chunk items (row by row), then
+  // whole rows class by class; position j of the list goes to workgroup j mod G on even
+  // rounds j / G and to G - 1 - j mod G on odd ones (a snake), so a workgroup that takes a
+  // heavy item early takes a light one late. Dealing items row by row instead put up to
+  // three long whole rows on one workgroup (mixed batch: 36 us of top-k on the slowest
+  // workgroup against a median of 20).
+  const uint32_t G = gridDim.x, g = blockIdx.x;
+  auto position = [&](uint32_t m) -> uint64_t { return (uint64_t)m * G + ((m & 1u) ? G - 1u - g : g); };
+  auto chunk_count = [&](int nv) { return chunks_of(p, nv); };
   Cursor cu;
   Item it;
-  // Phase 1a: histograms of this workgroup's chunks of several-chunk rows.
-  for (uint32_t item = blockIdx.x; locate(p, cu, sh, item, it); item += gridDim.x) {
-    if (it.nch == 1) continue;  // uniform
+  // Phase 1a: histograms of this workgroup's chunks of several-chunk rows (the chunk items
+  // come first in the list, so the numbering of chunk items alone finds them).
+  for (uint32_t m = 0;; ++m) {
+    if (!locate(p, cu, sh, (uint32_t)min<uint64_t>(position(m), 0xFFFFFFFFu), it, chunk_count)) break;
     float v[kChunkPer];
     fetch_chunk(p, it, v);
     for (int i = tid; i < kKeyBins; i += kCT) sh.hist[i] = 0;
@@ -866,11 +933,41 @@ __global__ __launch_bounds__(kCT) void topk_chunked_kernel(Params p) {
     __syncthreads();
     if (tid == 0) atomicAdd(&p.counters[4 * (int64_t)it.r + kCntHist], 1u);
   }
-  // Phase 1b: whole rows; trivial rows.
-  rewind(p, cu);
-  for (uint32_t item = blockIdx.x; locate(p, cu, sh, item, it); item += gridDim.x) {
-    if (it.nch != 1) continue;  // uniform
-    select_row_fit<kCT, kChunkCap, kWidePer>(p, it.r, it.nv, sh);
+  // Phase 1b: whole rows, class by class (their list positions follow the chunk items);
+  // trivial rows.
+  // The item totals, after the chunks are counted (before any wait on other workgroups).
+  const ItemTotals tot = item_totals(p, sh, cu);
+  {
+    const uint32_t nwhole = tot.whole[0] + tot.whole[1] + tot.whole[2] + tot.whole[3];
+    Cursor cw;
+    int cls_at = -1;  // class the cursor numbers
+    for (uint32_t m = 0;; ++m) {
+      const uint64_t j = position(m);
+      if (j < tot.chunks) continue;
+      uint32_t w = (uint32_t)(j - tot.chunks);
+      if (w >= nwhole) break;
+      // Class of list position w (w < nwhole), without indexing the totals (which would
+      // put them in memory).
+      int cls = 0;
+      if (w >= tot.whole[0]) {
+        w -= tot.whole[0];
+        cls = 1;
+        if (w >= tot.whole[1]) {
+          w -= tot.whole[1];
+          cls = 2;
+          if (w >= tot.whole[2]) {
+            w -= tot.whole[2];
+            cls = 3;
+          }
+        }
+      }
+      if (cls != cls_at) {  // a new numbering: start over
+        cw = Cursor();
+        cls_at = cls;
+      }
+      if (!locate(p, cw, sh, w, it, [&](int nv) { return whole_class(p, nv) == cls ? 1u : 0u; })) break;
+      select_row_fit<kCT, kChunkCap, kWidePer>(p, it.r, it.nv, sh);
+    }
   }
   for (int r = blockIdx.x; r < p.rows; r += gridDim.x) {
     const int nv = visible(p, r);
@@ -880,8 +977,9 @@ __global__ __launch_bounds__(kCT) void topk_chunked_kernel(Params p) {
   // again (mostly from cache) before the wait for its row's histogram, so the load and
   // the wait overlap.
   rewind(p, cu);
-  for (uint32_t item = blockIdx.x; locate(p, cu, sh, item, it); item += gridDim.x) {
-    if (it.nch == 1) continue;  // uniform
+  for (uint32_t m = 0;; ++m) {
+    const uint64_t j = position(m);
+    if (j >= tot.chunks || !locate(p, cu, sh, (uint32_t)j, it, chunk_count)) break;
     float v[kChunkPer];
     fetch_chunk(p, it, v);
     split_chunk(p, sh, it, v);
