@@ -26,6 +26,11 @@
 //     -inf tail that lie past each request's last stage.
 //     The balance does not depend on how context lengths are distributed, and nothing
 //     is read from the device by the host.
+//   * Small calls (a grid of at most one workgroup per CU that already holds a wave for
+//     every stage of every request at its largest context, up to 64 requests, one row
+//     group) skip the shares: wave gw owns stage gw / B of request gw % B, and loads that
+//     stage's table entries and its query rows together with the context lengths, so the
+//     first gathers wait for one round trip instead of two.
 //   * One wave owns a group of decode rows (at most 8 MFMA row tiles of 16 heads, 4 with
 //     64-token pages). Its query rows stay in VGPRs, already in f16, in the A-operand
 //     layout, for a whole segment. Decode rows beyond one wave's share are other row
