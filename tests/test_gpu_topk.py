@@ -158,3 +158,17 @@ def test_topk_workspace_reused_and_left_zero():
         run_case(L, k, specs, seed, ws=ws)
         nz = int(torch.count_nonzero(ws).item())
         assert nz == 0, f"L={L} k={k}: {nz} workspace bytes left nonzero"
+
+
+def test_topk_chunked_mode_more_rows_than_a_workgroup_scans():
+    """The chunked launch with more rows than one workgroup holds (1300 > 1024): the items
+    are numbered over several blocks of rows, and the whole rows of all four cost classes,
+    the trivial rows and a chunked row every hundred are dealt over many rounds."""
+    nvs = [5, 2048, 2049, 3000, 4096, 4097, 6000, 8192, 8193, 12000, 16384, 16385, 25000, 32768]
+    kinds = ["normal", "few", "narrow", "zeros", "inf"]
+    specs = []
+    for r in range(1300):
+        nv = (32769, 36000, 40000)[(r // 100) % 3] if r % 100 == 57 else nvs[r % len(nvs)]
+        specs.append((kinds[r % len(kinds)], nv))
+    say(f"[gpu] topk chunked mode, {len(specs)} rows, L=40000")
+    run_case(40000, 2048, specs, seed=7400)
