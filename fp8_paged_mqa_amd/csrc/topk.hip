@@ -572,10 +572,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_wide_kernel(Params p) {
 
 // ---- Chunked mode (max_model_len > kWideLen): one launch, no schedule pass.
 // Rows with k < nv <= kWideLen are one work item each (a whole-row select); rows longer
-// than that are cut into kChunk-element chunks, one item each. Items are numbered row by
-// row; item i belongs to workgroup i mod gridDim.x, and every workgroup derives the
-// numbering from context_lens itself. The grid is as many workgroups as fit on the GPU at
-// once (one per CU).
+// than that are cut into kChunk-element chunks, one item each. The items form one list,
+// heaviest first (the chunk items row by row, then the whole rows by cost class), dealt to
+// the workgroups in a snake; every workgroup derives the list from context_lens itself.
+// The grid is as many workgroups as fit on the GPU at once (one per CU).
 //   Phase 1, no waiting: for each of its chunks of a long row, a workgroup adds the
 //   chunk's 12-bit key histogram into the row's histogram (global atomics) and then counts
 //   the chunk; it selects its whole rows; it writes its trivial rows.
