@@ -62,6 +62,7 @@ constexpr int kChunk = kChunkThreads * kChunkPer; // 8192-element chunks
 constexpr int kLinBins = 2048;                    // first level of a whole-row select (linear)
 constexpr int kKeyBits = 12;                      // first level of a chunked row (top key bits)
 constexpr int kKeyBins = 1 << kKeyBits;           // 4096
+constexpr int kCoarseBins = 64;                   // chunked rows: top 6 key bits, 64 key bins each
 constexpr int kRowCap = 8192;                     // LDS candidates of a whole-row select (64 KB)
 constexpr int kChunkCap = kRowCap;                // LDS (and workspace) candidates of a chunked row
 constexpr int kRankMax = 256;                     // candidate lists up to this size are ranked
@@ -73,6 +74,7 @@ struct Params {
   // Workspace of the chunked mode (null otherwise), zero between calls: per row r,
   uint32_t* counters;     // [rows][4]: chunk histograms added, chunks split, emitted, candidates
   uint32_t* hist;         // [rows][kKeyBins] 12-bit key histogram
+  uint32_t* coarse;       // [rows][kCoarseBins] the same counts over the top 6 key bits
   uint64_t* cand;         // [rows][kChunkCap] threshold-bin candidates
   int32_t rows, N, W, L, k;
 };
@@ -105,7 +107,7 @@ struct Core {
   static constexpr int kWaves = T / 64;
   uint32_t hist[kKeyBins];
   uint32_t red[kRedGroups * kWaves];
-  uint32_t n_out, bin, above, base_a, base_b, last;
+  uint32_t n_out, bin, above, base_a, base_b, last, count;
   int32_t loc[4];  // the chunk located last: row, chunk, visible, chunks of the row
 };
 
@@ -759,6 +761,7 @@ __device__ void finish_row(const Params& p, ChunkFull& sh, const Item& it, uint3
   }
   uint4* gh = reinterpret_cast<uint4*>(p.hist + (int64_t)it.r * kKeyBins);
   for (int i = threadIdx.x; i < kKeyBins / 4; i += kCT) gh[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x < kCoarseBins) p.coarse[(int64_t)it.r * kCoarseBins + threadIdx.x] = 0u;
   if (threadIdx.x < 4) store_agent(p.counters + 4 * (int64_t)it.r + threadIdx.x, 0u);
 }
 
@@ -778,17 +781,37 @@ __device__ void split_chunk(const Params& p, ChunkFull& sh, const Item& it, cons
     sh.last = polls < kWaitPolls ? 1u : 0u;
   }
   __syncthreads();
+  uint32_t bin0, above, cnt0;
   if (sh.last) {  // uniform
-    const uint64_t* gh = reinterpret_cast<const uint64_t*>(p.hist + (int64_t)it.r * kKeyBins);
-    uint64_t* lh = reinterpret_cast<uint64_t*>(sh.hist);
-#pragma unroll
-    for (int i = 0; i < kKeyBins / 2 / kCT; ++i) lh[i * kCT + tid] = load_agent(gh + i * kCT + tid);
+    // The threshold bin from the row's coarse counts, then from the 64 key bins of the
+    // coarse bin holding it: wave 0, two loads of 256 bytes (lane l reads the l-th bin from
+    // the top), no scan of the 4096 bins. The row holds more than k visible elements, so
+    // both searches end inside their bins.
+    if (wave == 0) {
+      const uint32_t cc = load_agent(p.coarse + (int64_t)it.r * kCoarseBins + (kCoarseBins - 1 - lane));
+      const uint32_t cincl = wave_scan_add(cc);
+      const int ol = __builtin_ctzll(__ballot(cincl >= (uint32_t)k));
+      const uint32_t above_c = (uint32_t)__builtin_amdgcn_readlane((int)(cincl - cc), ol);
+      const int cb = kCoarseBins - 1 - ol;
+      const uint32_t fc = load_agent(p.hist + (int64_t)it.r * kKeyBins + cb * 64 + (63 - lane));
+      const uint32_t fincl = wave_scan_add(fc);
+      const int fl = __builtin_ctzll(__ballot(above_c + fincl >= (uint32_t)k));
+      const uint32_t above_f = (uint32_t)__builtin_amdgcn_readlane((int)(fincl - fc), fl);
+      const uint32_t count_f = (uint32_t)__builtin_amdgcn_readlane((int)fc, fl);
+      if (lane == 0) {
+        sh.bin = (uint32_t)(cb * 64 + 63 - fl);
+        sh.above = above_c + above_f;
+        sh.count = count_f;
+      }
+    }
     __syncthreads();
+    bin0 = sh.bin;
+    above = sh.above;
+    cnt0 = sh.count;
   } else {
     build_row_hist(p, sh, it);
+    threshold_bin<kCT, kKeyBins / kCT>(sh, (uint32_t)k, bin0, above, cnt0);
   }
-  uint32_t bin0, above, cnt0;
-  threshold_bin<kCT, kKeyBins / kCT>(sh, (uint32_t)k, bin0, above, cnt0);
   const bool whole = cnt0 == (uint32_t)k - above;
   // Elements above the threshold bin (the whole bin too when all of it is taken) go to
   // the output, the bin's own elements to the row's candidate list; slots from one pair
@@ -924,9 +947,14 @@ __global__ __launch_bounds__(kCT) void topk_chunked_kernel(Params p) {
     count_chunk(sh, it, v);
     __syncthreads();
     uint32_t* gh = p.hist + (int64_t)it.r * kKeyBins;
+    uint32_t* gc = p.coarse + (int64_t)it.r * kCoarseBins;
+    static_assert(kKeyBins / kCoarseBins == 64 && kKeyBins % kCT == 0, "a wave's 64 lanes hold one coarse bin's key bins");
     for (int i = tid; i < kKeyBins; i += kCT) {
       const uint32_t c = sh.hist[i];
       if (c) atomicAdd(&gh[i], c);
+      // The 64 lanes of a wave hold the 64 key bins of coarse bin i / 64.
+      const uint32_t cs = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_add(c), 63);
+      if ((tid & 63) == 0 && cs) atomicAdd(&gc[i >> 6], cs);
     }
     // Count the chunk once its histogram has reached the row's (atomics complete).
     __builtin_amdgcn_s_waitcnt(0);
@@ -987,10 +1015,10 @@ __global__ __launch_bounds__(kCT) void topk_chunked_kernel(Params p) {
 }
 
 // Workspace layout (chunked mode): counters [rows][4] u32 | hist [rows][kKeyBins] u32 |
-// cand [rows][kChunkCap] u64; every region 16-byte aligned (the histograms are cleared as
-// uint4; the workspace base is 16-byte aligned).
+// coarse [rows][kCoarseBins] u32 | cand [rows][kChunkCap] u64; every region 16-byte aligned
+// (the histograms are cleared as uint4; the workspace base is 16-byte aligned).
 struct Layout {
-  size_t counters, hist, cand, total;
+  size_t counters, hist, coarse, cand, total;
 };
 
 Layout layout(int64_t rows) {
@@ -998,7 +1026,8 @@ Layout layout(int64_t rows) {
   Layout l;
   l.counters = 0;
   l.hist = (size_t)16 * rows;
-  l.cand = l.hist + (size_t)4 * kKeyBins * rows;
+  l.coarse = l.hist + (size_t)4 * kKeyBins * rows;
+  l.cand = l.coarse + (size_t)4 * kCoarseBins * rows;
   l.total = l.cand + (size_t)8 * kChunkCap * rows;
   return l;
 }
@@ -1084,6 +1113,7 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   p.counters = reinterpret_cast<uint32_t*>(ws + l.counters);
   p.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
+  p.coarse = reinterpret_cast<uint32_t*>(ws + l.coarse);
   p.cand = reinterpret_cast<uint64_t*>(ws + l.cand);
   // Every workgroup resident at once (the waits assume it; see above), and no more than
   // the chunks can need (every row at its longest).
