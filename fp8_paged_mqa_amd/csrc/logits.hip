@@ -26,7 +26,7 @@
 //     -inf tail that lie past each request's last stage.
 //     The balance does not depend on how context lengths are distributed, and nothing
 //     is read from the device by the host.
-//   * Small calls (a grid of at most one workgroup per CU that already holds a wave for
+//   * Small calls (a grid of at most two workgroups per CU that already holds a wave for
 //     every stage of every request at its largest context, up to 64 requests, one row
 //     group) skip the shares: wave gw owns stage gw / B of request gw % B, and loads that
 //     stage's table entries and its query rows together with the context lengths, so the
@@ -50,6 +50,12 @@
 //     unconditionally (a dead stage or a table entry outside the cache reads row 0
 //     instead), and the prologue issues in the loop's order, so the loop is
 //     straight-line code and each compute waits only for its own stage's loads.
+//   * Half-stage form (pages under 64 tokens, one row group, up to 64 heads, a wave
+//     holding several decode rows): the two 32-token halves of the next stage are in
+//     flight (~8.4 KB) while a stage is computed, the weights sit in LDS, and one tile's
+//     operands and accumulators are live at a time, so even 8 row tiles fit 256 VGPRs
+//     and two workgroups share a CU: the same bytes in flight per CU, spread over twice
+//     the waves.
 //   * Epilogue in registers: the dequant scale's sign is folded into the fp8 key (flip
 //     the sign bit of every byte, exact; skipped when no scale of the tile is negative),
 //     so relu(scale*s) = |scale| * relu(sign*s) and |scale| multiplies once per token
@@ -140,12 +146,14 @@ __device__ __forceinline__ Operand to_operand(i32x4 lo, i32x4 hi) {
   return o;
 }
 
-// Gathered keys of one 64-token stage, in the lane's B-operand slots.
-struct Stage {
-  i32x4 lo[kTilesPerStage];
-  i32x4 hi[kTilesPerStage];
-  float scale[kTilesPerStage];
-  int phys[kTilesPerStage];
+// Gathered keys of NT consecutive 16-token column tiles (a whole stage, NT = 4, or half
+// of one, NT = 2), in the lane's B-operand slots.
+template <int NT>
+struct Keys {
+  i32x4 lo[NT];
+  i32x4 hi[NT];
+  float scale[NT];
+  int bad;  // bit u: tile u's table entry is outside the cache (its row 0 was read)
 };
 
 // x summed over the four lane groups {c, c+16, c+32, c+48}; every lane gets the sum
@@ -199,12 +207,14 @@ __device__ __forceinline__ int locate(const int* a, int n, int x) {
   return lo;
 }
 
-// Up to 4 row tiles fit two waves per SIMD (<= 256 VGPRs); the 5..8-tile variants (H > 64,
-// or several decode rows per wave with pages under 64 tokens) take the whole register file.
-template <int TPJ, int JPG, bool SMALL>
-__global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logits_kernel(Params p) {
+// Up to 4 row tiles fit two waves per SIMD (<= 256 VGPRs); so do up to 8 in the half-stage
+// form (HALF: half a stage of keys per pipeline slot, weights in LDS). The other 5..8-tile
+// variants (H > 64, or several decode rows per wave) take the whole register file.
+template <int TPJ, int JPG, bool SMALL, bool HALF>
+__global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4 || HALF) ? 2 : 1) void paged_logits_kernel(Params p) {
   constexpr int TILES = TPJ * JPG;  // MFMA row tiles (16 heads each) held by one wave
   static_assert(TILES >= 1 && TILES <= 8, "query tile budget");
+  static_assert(!(SMALL && HALF), "one form per instance");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -213,6 +223,7 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   // the tail-chunk prefix and scan scratch. Up to 64, every wave keeps them in registers
   // (one request per lane, no barrier) and LDS is not used.
   extern __shared__ int lds[];
+  __shared__ f32x4 wsh[HALF ? kWavesPerGroup : 1][HALF ? TILES : 1][4];  // half form: weights per wave
   const int B = p.B;
   const bool per_wave = B <= kWave;
   int* ctx_s = lds;                     // [B]
@@ -341,39 +352,41 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
   const uint8_t* kv_g = p.kv + 16 * g;  // this lane's first key slice
   const uint8_t* kv_s = p.kv + kD;      // scales
   {
-    // One 64-token stage starting at token tok0 of the request whose table entries (lane l:
-    // the entry of token tok0 + l) are in tab: its rows' keys into the B-operand slots of s
-    // (row 0 when the stage is not live or an entry is outside the cache).
-    auto gather_stage = [&](int tok0, bool live, int tab, Stage& s) {
-      int ph[kTilesPerStage];
+    // NT column tiles u0 .. u0+NT-1 of the stage starting at token tok0, whose table entries
+    // (lane l: the entry of token tok0 + l) are in tab: their rows' keys into the B-operand
+    // slots of s (row 0 when the stage is not live or an entry is outside the cache).
+    auto gather_tiles = [&](int tok0, int u0, bool live, int tab, auto& s) {
+      constexpr int NT = sizeof(s.scale) / sizeof(float);
+      int ph[NT];
 #pragma unroll
-      for (int u = 0; u < kTilesPerStage; ++u) ph[u] = __shfl(tab, u * 16 + c);
+      for (int u = 0; u < NT; ++u) ph[u] = __shfl(tab, (u0 + u) * 16 + c);
       const uint32_t smask = (1u << p.bshift) - 1u;  // slot of a token in its block
       const uint32_t tok = (uint32_t)(tok0 + c);
+      s.bad = 0;
 #pragma unroll
-      for (int u = 0; u < kTilesPerStage; ++u) {
-        const uint32_t slot = (tok + 16u * u) & smask;
-        const uint32_t row = (live && (uint32_t)ph[u] < p.nblk) ? ((uint32_t)ph[u] << p.bshift) | slot : 0u;
+      for (int u = 0; u < NT; ++u) {
+        const uint32_t slot = (tok + 16u * (u0 + u)) & smask;
+        const bool inb = (uint32_t)ph[u] < p.nblk;
+        const uint32_t row = (live && inb) ? ((uint32_t)ph[u] << p.bshift) | slot : 0u;
+        s.bad |= (inb ? 0 : 1) << u;
         const uint8_t* kp = kv_g + (uint64_t)row * kRow;
-        s.phys[u] = ph[u];
         s.lo[u] = load16(kp);
         s.hi[u] = load16(kp + 64);
         s.scale[u] = *reinterpret_cast<const float*>(kv_s + (uint64_t)row * kRow);
       }
     };
-    // The stage at token tc: contraction, epilogue and the stores of its 64 logits for the
-    // jn owned decode rows (row jl of out0 + jl * L; positions from t_need on are past ctx,
-    // from nv[jl] on past the row's causal limit, from t_end on past the output row).
-    auto compute_stage = [&](const Operand (&qa)[TILES], const f32x4 (&wv)[TILES], const Stage& s, int tc,
-                             int t_need, int t_end, const int (&nv)[JPG], float* out0, int jn) {
-      float keep[JPG];
+    // Contraction and epilogue of those tiles of the stage at token tc for the owned decode
+    // rows: lane group g keeps row jl's head sum of tile g in keep[jl] (positions from
+    // t_need on are past ctx). wget(m) gives the lane's weights of row tile m.
+    auto compute_tiles = [&](const Operand (&qa)[TILES], auto&& wget, const auto& s, int tc, int u0, int t_need,
+                             float (&keep)[JPG]) {
+      constexpr int NT = sizeof(s.scale) / sizeof(float);
 #pragma unroll
-      for (int jl = 0; jl < JPG; ++jl) keep[jl] = 0.0f;
-#pragma unroll
-      for (int u = 0; u < kTilesPerStage; ++u) {
-        const int t = tc + u * 16 + c;
+      for (int u = 0; u < NT; ++u) {
+        const int ug = u0 + u;
+        const int t = tc + ug * 16 + c;
         const bool in_ctx = t < t_need;
-        const bool ok = in_ctx && (uint32_t)s.phys[u] < p.nblk;
+        const bool ok = in_ctx && !((s.bad >> u) & 1);
         // Past ctx the column is masked below; a bad table entry poisons it with NaN.
         const float sc = ok ? s.scale[u] : (in_ctx ? __builtin_nanf("") : 0.0f);
         i32x4 lo = s.lo[u], hi = s.hi[u];
@@ -384,28 +397,36 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         }
         const Operand kb = to_operand(lo, hi);
         const float sabs = __builtin_fabsf(sc);
-        f32x4 acc[TILES];
-#pragma unroll
-        for (int m = 0; m < TILES; ++m) {
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[0], kb.k[0], f32x4{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-          for (int k = 1; k < 4; ++k)
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[k], kb.k[k], acc[m], 0, 0, 0);
-        }
 #pragma unroll
         for (int jl = 0; jl < JPG; ++jl) {
-          float part = 0.0f;
+          f32x4 acc[TPJ];
 #pragma unroll
           for (int mm = 0; mm < TPJ; ++mm) {
             const int m = jl * TPJ + mm;
+            acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[0], kb.k[0], f32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+            for (int k = 1; k < 4; ++k)
+              acc[mm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[m].k[k], kb.k[k], acc[mm], 0, 0, 0);
+          }
+          float part = 0.0f;
+#pragma unroll
+          for (int mm = 0; mm < TPJ; ++mm) {
+            const f32x4 wm = wget(jl * TPJ + mm);
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              part = __builtin_fmaf(wv[m][v], __builtin_elementwise_maximum(acc[m][v], 0.0f), part);
+              part = __builtin_fmaf(wm[v], __builtin_elementwise_maximum(acc[mm][v], 0.0f), part);
           }
           part = sum_lane_groups(part);
-          if (g == u) keep[jl] = part * sabs;
+          if (g == ug) keep[jl] = part * sabs;
         }
+        // The half form keeps one tile's operands and accumulators live at a time: its
+        // register budget is that of two waves per SIMD.
+        if constexpr (HALF) __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    // The stage's 64 logits of the jn owned decode rows (row jl of out0 + jl * L; positions
+    // from nv[jl] on are past the row's causal limit, from t_end on past the output row).
+    auto store_stage = [&](int tc, int t_end, const int (&nv)[JPG], float* out0, int jn, const float (&keep)[JPG]) {
       const int t = tc + lane;  // lane (g, c) stores token 16g + c of the stage
       if (t < t_end) {
 #pragma unroll
@@ -422,12 +443,16 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         int nv[JPG];
 #pragma unroll
         for (int jl = 0; jl < JPG; ++jl) nv[jl] = min(ctx - p.N + jl + 1, L);
-        Stage sx;
-        gather_stage(tc, true, tab_s, sx);
+        Keys<kTilesPerStage> sx;
+        gather_tiles(tc, 0, true, tab_s, sx);
         Operand qs[TILES];
 #pragma unroll
         for (int m = 0; m < TILES; ++m) qs[m] = to_operand(qraw_s[m][0], qraw_s[m][1]);
-        compute_stage(qs, wv_s, sx, tc, t_need, t_end, nv, p.out + (int64_t)sb * p.N * L, min(JPG, p.N));
+        float keep[JPG];
+#pragma unroll
+        for (int jl = 0; jl < JPG; ++jl) keep[jl] = 0.0f;
+        compute_tiles(qs, [&](int m) { return wv_s[m]; }, sx, tc, 0, t_need, keep);
+        store_stage(tc, t_end, nv, p.out + (int64_t)sb * p.N * L, min(JPG, p.N), keep);
       }
     } else if (wi < nw) {
     int lo = wi * sq + (wi * sr) / nw;
@@ -476,48 +501,91 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
         {
           const uint8_t* qb = p.q + ((int64_t)b * p.N + j0) * p.H * kD;
           const float* wb = p.w + ((int64_t)b * p.N + j0) * p.H;
+          // Row tiles of decode rows past N repeat the last row (never stored).
+          auto row_tile = [&](int m) { return min(m / TPJ, jn - 1) * TPJ + m % TPJ; };
+#pragma unroll
+          for (int m = 0; m < TILES; ++m) wv[m] = *reinterpret_cast<const f32x4*>(wb + row_tile(m) * 16 + 4 * g);
 #pragma unroll
           for (int m = 0; m < TILES; ++m) {
-            // Row tiles of decode rows past N repeat the last row (never stored).
-            const int mr = min(m / TPJ, jn - 1) * TPJ + m % TPJ;
-            const uint8_t* qr = qb + (mr * 16 + c) * kD;
+            const uint8_t* qr = qb + (row_tile(m) * 16 + c) * kD;
             qraw[m][0] = load16(qr + 16 * g);
             qraw[m][1] = load16(qr + 64 + 16 * g);
-            wv[m] = *reinterpret_cast<const f32x4*>(wb + mr * 16 + 4 * g);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
         Operand qa[TILES];
 
-        auto issue_keys = [&](int st, int tab, Stage& s) { gather_stage(t0 + st * kStage, st < nstage, tab, s); };
-
-        auto compute_store = [&](int st, const Stage& s) {
-          compute_stage(qa, wv, s, t0 + st * kStage, t_need, t_end, nv, out0, jn);
-        };
-
-        // Software pipeline: keys of two stages in flight, table entries two stages ahead
-        // of their use; the compute of stage s waits only for stage s's loads, and its
-        // registers are refilled with stage s+2 right after.
-        // The prologue issues in the loop's order (keys of a stage, then the table entries
-        // two stages on), so the wait counts computed for the loop's first pass hold for
-        // every pass; stages past the segment issue harmless loads of row 0, so the loop
-        // body is straight-line code. sched_barrier(0) keeps the scheduler from pulling a
-        // use of a load up next to it, which would serialise the latencies.
-        Stage sa, sb;
-        issue_keys(0, tab0, sa);
-        tab0 = load_table(2);
-        issue_keys(1, tab1, sb);
-        tab1 = load_table(3);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!HALF) {
+          // Software pipeline: keys of two stages in flight, table entries two stages ahead
+          // of their use; the compute of stage s waits only for stage s's loads, and its
+          // registers are refilled with stage s+2 right after.
+          // The prologue issues in the loop's order (keys of a stage, then the table entries
+          // two stages on), so the wait counts computed for the loop's first pass hold for
+          // every pass; stages past the segment issue harmless loads of row 0, so the loop
+          // body is straight-line code. sched_barrier(0) keeps the scheduler from pulling a
+          // use of a load up next to it, which would serialise the latencies.
+          auto issue_keys = [&](int st, int tab, Keys<kTilesPerStage>& s) {
+            gather_tiles(t0 + st * kStage, 0, st < nstage, tab, s);
+          };
+          auto compute_store = [&](int st, const Keys<kTilesPerStage>& s) {
+            float keep[JPG];
 #pragma unroll
-        for (int m = 0; m < TILES; ++m) qa[m] = to_operand(qraw[m][0], qraw[m][1]);
-        for (int st = 0; st < nstage; st += 2) {
-          compute_store(st, sa);
-          issue_keys(st + 2, tab0, sa);
-          tab0 = load_table(st + 4);
-          if (st + 1 < nstage) compute_store(st + 1, sb);
-          issue_keys(st + 3, tab1, sb);
-          tab1 = load_table(st + 5);
+            for (int jl = 0; jl < JPG; ++jl) keep[jl] = 0.0f;
+            compute_tiles(qa, [&](int m) { return wv[m]; }, s, t0 + st * kStage, 0, t_need, keep);
+            store_stage(t0 + st * kStage, t_end, nv, out0, jn, keep);
+          };
+          Keys<kTilesPerStage> sa, sb;
+          issue_keys(0, tab0, sa);
+          tab0 = load_table(2);
+          issue_keys(1, tab1, sb);
+          tab1 = load_table(3);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int m = 0; m < TILES; ++m) qa[m] = to_operand(qraw[m][0], qraw[m][1]);
+          for (int st = 0; st < nstage; st += 2) {
+            compute_store(st, sa);
+            issue_keys(st + 2, tab0, sa);
+            tab0 = load_table(st + 4);
+            if (st + 1 < nstage) compute_store(st + 1, sb);
+            issue_keys(st + 3, tab1, sb);
+            tab1 = load_table(st + 5);
+          }
+        } else {
+          // Half-stage pipeline: the two halves (32 tokens each) of the next stage are in
+          // flight while a stage is computed, and table entries are loaded two stages
+          // ahead of their use; the prologue issues in the loop's order here too. Half the
+          // key registers of the form above, so two workgroups fit on a CU with the same
+          // bytes in flight per CU. The weights wait in this wave's LDS slots (read back as
+          // broadcasts) instead of 4 * TILES VGPRs.
+          Keys<2> sa, sb;
+          int tn = tab0;   // entries of the stage whose halves are issued next
+          int tnn = tab1;  // and of the one after it
+          gather_tiles(t0, 0, 0 < nstage, tn, sa);
+          gather_tiles(t0, 2, 0 < nstage, tn, sb);
+          tn = tnn;
+          tnn = load_table(2);
+          __builtin_amdgcn_sched_barrier(0);
+          if (c == 0) {
+#pragma unroll
+            for (int m = 0; m < TILES; ++m) wsh[wave][m][g] = wv[m];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int m = 0; m < TILES; ++m) qa[m] = to_operand(qraw[m][0], qraw[m][1]);
+          auto wget = [&](int m) { return wsh[wave][m][g]; };
+          for (int st = 0; st < nstage; ++st) {
+            const int tc = t0 + st * kStage;
+            float keep[JPG];
+#pragma unroll
+            for (int jl = 0; jl < JPG; ++jl) keep[jl] = 0.0f;
+            compute_tiles(qa, wget, sa, tc, 0, t_need, keep);
+            gather_tiles(tc + kStage, 0, st + 1 < nstage, tn, sa);
+            compute_tiles(qa, wget, sb, tc, 2, t_need, keep);
+            store_stage(tc, t_end, nv, out0, jn, keep);
+            gather_tiles(tc + kStage, 2, st + 1 < nstage, tn, sb);
+            tn = tnn;
+            tnn = load_table(st + 3);
+          }
         }
       }
 
@@ -594,9 +662,11 @@ __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4) ? 2 : 1) void paged_logi
 using KernelFn = void (*)(Params);
 
 template <int TPJ, int JPG>
-constexpr KernelFn kfn() { return paged_logits_kernel<TPJ, JPG, false>; }
+constexpr KernelFn kfn() { return paged_logits_kernel<TPJ, JPG, false, false>; }
 template <int TPJ, int JPG>
-constexpr KernelFn kfs() { return paged_logits_kernel<TPJ, JPG, true>; }
+constexpr KernelFn kfs() { return paged_logits_kernel<TPJ, JPG, true, false>; }
+template <int TPJ, int JPG>
+constexpr KernelFn kfh() { return paged_logits_kernel<TPJ, JPG, false, true>; }
 
 // [TPJ-1][JPG-1]; TPJ = H/16 in 1..8, JPG = decode rows per wave: min(N, T/TPJ) with
 // T = 8 row tiles (128 f16 query VGPRs) for pages under 64 tokens and T = 4 (64 VGPRs,
@@ -618,6 +688,14 @@ constexpr KernelFn kTableSmall[4][4] = {
     {kfs<2, 1>(), kfs<2, 2>(), nullptr, nullptr},
     {kfs<3, 1>(), nullptr, nullptr, nullptr},
     {kfs<4, 1>(), nullptr, nullptr, nullptr},
+};
+
+// Half-stage forms, [TPJ-1][JPG-1] for up to 64 heads and several decode rows per wave.
+constexpr KernelFn kTableHalf[4][4] = {
+    {nullptr, kfh<1, 2>(), kfh<1, 3>(), kfh<1, 4>()},
+    {nullptr, kfh<2, 2>(), kfh<2, 3>(), kfh<2, 4>()},
+    {nullptr, kfh<3, 2>(), nullptr, nullptr},
+    {nullptr, kfh<4, 2>(), nullptr, nullptr},
 };
 
 // Compute units of the current device, read once per device.
@@ -668,29 +746,41 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   p.vec_store = (a.max_model_len % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
   KernelFn fn = kTable[tpj - 1][jpg - 1];
   const size_t lds = logits_lds_bytes(a.batch);
-  // One round of persistent workgroups, one per CU, but no more waves than there can be
-  // work for: the host knows an upper bound of the key stages (every request at its
+  // One round of persistent workgroups, one or two per CU, but no more waves than there
+  // can be work for: the host knows an upper bound of the key stages (every request at its
   // largest context) and of the tail chunks, and small calls then launch a small grid.
-  // Four waves per CU measured faster than eight (two workgroups) on single-token pages
-  // and on single-group calls: each wave takes twice the stages and pays the start-up -
-  // schedule, table and query loads queued behind the other waves' gathers - half as
-  // often. With 64-token pages and several query groups per request (every key stage read
-  // once per group, the later reads mostly from L2) eight waves per CU were faster (4 to
-  // 10%): the key reads are whole lines and the wave is waiting on latency, not on HBM.
-  // Two waves per CU, or a deeper prefetch (three or four stages in flight per wave), were
-  // slower everywhere.
   const int64_t ctx_cap = a.max_model_len < (int64_t)p.Wt ? a.max_model_len : (int64_t)p.Wt;
   const int64_t stage_bound = (int64_t)a.batch * ((ctx_cap + kStage - 1) / kStage + kStartUnits) * p.groups;
   const int64_t tail_bound = (int64_t)a.batch * a.next_n * ((a.max_model_len + kTailChunk - 1) / kTailChunk);
   const int64_t need = (std::max(stage_bound, tail_bound) + kWavesPerGroup - 1) / kWavesPerGroup;
-  const int64_t per_cu = (a.block_shift >= 6 && p.groups > 1 && tpj * jpg <= 4) ? 2 : 1;
-  const int64_t full = per_cu * compute_units();
-  const int blocks = (int)std::max<int64_t>(1, std::min(full, need));
-  // Small calls: when that grid holds a wave for every stage of every request at its largest
-  // context (one row group, at most 64 requests), each wave takes one stage, fixed by its
-  // index, and issues its table and query loads beside the context lengths: the schedule's
-  // round trips (context lengths, then table entries, then keys) become one.
-  if (a.batch <= kWave && p.groups == 1 && tpj * jpg <= 4 && need <= full) fn = kTableSmall[tpj - 1][jpg - 1];
+  const int cus = compute_units();
+  int64_t per_cu = 1;
+  if (a.batch <= kWave && p.groups == 1 && tpj * jpg <= 4 && need <= 2 * (int64_t)cus) {
+    // Small calls: when two workgroups per CU hold a wave for every stage of every request
+    // at its largest context (one row group, at most 64 requests), each wave takes one
+    // stage, fixed by its index, and issues its table and query loads beside the context
+    // lengths: the schedule's round trips (context lengths, then table entries, then keys)
+    // become one.
+    fn = kTableSmall[tpj - 1][jpg - 1];
+    per_cu = 2;
+  } else if (a.block_shift < 6 && p.groups == 1 && jpg > 1) {
+    // A wave holding several decode rows (pages under 64 tokens, up to 64 heads): the
+    // half-stage form, whose registers fit two workgroups per CU; with whole stages its
+    // query and key registers take the whole register file, one wave per SIMD.
+    fn = kTableHalf[tpj - 1][jpg - 1];
+    per_cu = 2;
+  } else if (a.block_shift >= 6 && p.groups > 1 && tpj * jpg <= 4) {
+    // With whole stages, four waves per CU measured faster than eight on single-token pages
+    // and on single-group calls: each wave takes twice the stages and pays the start-up -
+    // schedule, table and query loads queued behind the other waves' gathers - half as
+    // often. With 64-token pages and several query groups per request (every key stage
+    // read once per group, the later reads mostly from L2) eight waves per CU were faster
+    // (4 to 10%): the key reads are whole lines and the wave is waiting on latency, not on
+    // HBM. Two waves per CU, or a deeper prefetch (three or four stages in flight per
+    // wave), were slower everywhere.
+    per_cu = 2;
+  }
+  const int blocks = (int)std::max<int64_t>(1, std::min(per_cu * cus, need));
   hipLaunchKernelGGL(fn, dim3(blocks), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }

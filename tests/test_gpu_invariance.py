@@ -57,6 +57,23 @@ def test_small_call_rows_match_large_call_bitwise():
         assert np.all(full[b, 4096:] == -np.inf)
 
 
+def test_two_workgroup_small_call_rows_match_scheduled_rows_bitwise():
+    """Twelve requests of at most 8192 positions: with max_model_len 8192 two workgroups per
+    CU hold a wave for each of their stages (the small-call form, waves past 1024 too); with
+    max_model_len 65536 the call runs in scheduled whole stages. Same bits on the first 8192
+    positions, -inf after."""
+    ctx = [1, 63, 64, 65, 2047, 2048, 2049, 4097, 8192, 5000, 700, 33]
+    case = wl.make_case(batch=len(ctx), next_n=1, heads=64, ctx=ctx, max_model_len=8192, seed=55)
+    half, ih = run_gpu(case)
+    bt = np.full((case.batch, 65536), -1, dtype=np.int32)  # a table as wide as the rows
+    bt[:, :case.block_tables.shape[1]] = case.block_tables
+    longer = wl.Workload("longer", case.q, case.kv_cache, case.weights, case.context_lens, bt, 65536, 1)
+    whole, iw = run_gpu(longer)
+    assert np.array_equal(half.view(np.uint32), whole[:, :8192].view(np.uint32))
+    assert np.all(whole[:, 8192:] == -np.inf)
+    assert np.array_equal(np.sort(ih, axis=1), np.sort(iw, axis=1))
+
+
 def test_repeatable():
     case = wl.make_named("mtp_b32_n2_ctx32k")
     g1, i1 = run_gpu(case)
@@ -209,12 +226,15 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("next_n,heads", [(2, 64), (4, 32)])
 @pytest.mark.parametrize("block_size", [16, 64])
-def test_block_size_identity_bitwise(block_size):
+def test_block_size_identity_bitwise(block_size, next_n, heads):
     """A cache in blocks of S (permuted blocks) gives bit-identical logits and the same
-    selections as a block_size 1 cache holding each token's row behind a per-token table."""
-    case = wl.make_case(batch=4, next_n=2, heads=64, ctx=[5, 1000, 2049, 4097], max_model_len=4100,
-                        seed=61 + block_size, block_size=block_size, pool=600)
+    selections as a block_size 1 cache holding each token's row behind a per-token table.
+    With S = 64 the decode rows are split over row groups in whole stages; with S = 16 and
+    S = 1 one wave holds all of them, in half stages."""
+    case = wl.make_case(batch=4, next_n=next_n, heads=heads, ctx=[5, 1000, 2049, 4097], max_model_len=4100,
+                        seed=61 + block_size + next_n, block_size=block_size, pool=600)
     gS, iS = run_gpu(case)
     rows = case.kv_cache.reshape(-1, 132)
     bt1 = np.full((case.batch, 4100), -1, dtype=np.int32)
