@@ -15,8 +15,8 @@
 //     converted exactly to f16 (v_cvt_scalef32_pk_f16_fp8, scale 1) and contracted with
 //     v_mfma_f32_16x16x32_f16, four chained per 128-wide row: f16 products of e4m3
 //     values are exact and the fp32 accumulation is correctly rounded.
-//   * Schedule: one round of persistent workgroups (one per CU), so no workgroup waits
-//     for a slot. Each wave scans context_lens into prefix sums (for up to 64 requests
+//   * Schedule: one round of persistent workgroups (one or two per CU), so no workgroup
+//     waits for a slot. Each wave scans context_lens into prefix sums (for up to 64 requests
 //     in its own registers, one request per lane, no barrier or LDS; beyond that in LDS,
 //     one copy per workgroup, DPP wave scans and one barrier); every
 //     wave then takes an equal contiguous share of the work units of all requests -
@@ -721,9 +721,10 @@ size_t logits_lds_bytes(int32_t batch) {
 hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
   const int tpj = a.heads / 16;
   // Decode rows per wave: with pages under 64 tokens a wave holds up to 8 row tiles, so
-  // the key rows of a stage are gathered once for all of a request's decode rows (one
-  // four-wave workgroup per CU leaves each wave the whole register file); with 64-token
-  // pages up to 4, so that two workgroups fit on a CU (measured faster there for N = 4).
+  // the key rows of a stage are gathered once for all of a request's decode rows (in the
+  // half-stage form below, two workgroups per CU); with 64-token pages up to 4, in whole
+  // stages, two workgroups per CU when a request has several row groups (measured faster
+  // there for N = 4).
   const int max_tiles = a.block_shift < 6 ? 8 : 4;
   const int per_wave = tpj <= max_tiles ? max_tiles / tpj : 1;
   const int jpg = a.next_n < per_wave ? a.next_n : per_wave;

@@ -580,12 +580,15 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_wide_kernel(Params p) {
 // The grid is as many workgroups as fit on the GPU at once (one per CU).
 //   Phase 1, no waiting: for each of its chunks of a long row, a workgroup adds the
 //   chunk's 12-bit key histogram into the row's histogram (global atomics) and then counts
-//   the chunk; it selects its whole rows; it writes its trivial rows.
+//   the chunk.
 //   Phase 2: for each of its chunks of a several-chunk row, it waits until the row's count
 //   shows every chunk's histogram, takes the threshold bin from the row's histogram, emits
 //   the chunk's elements above it and collects those in it into the row's candidate list;
 //   the workgroup that counts a row's last chunk finishes the row's candidates and returns
 //   the row's workspace to zero, so the next call needs no clearing pass or memset.
+//   Phase 3, no waiting: it selects its whole rows and writes its trivial rows. Coming
+//   after the splits, the row finishes (which the snake does not weigh) run while other
+//   workgroups still select whole rows, instead of after the heaviest of them.
 // A wait only ever waits for phase-1 work, and phase 1 never waits, so with every
 // workgroup resident the waits end; the wait is bounded all the same, and a workgroup whose
 // wait runs out builds the row's histogram from the row itself (the same counts, so the
@@ -936,7 +939,7 @@ __global__ __launch_bounds__(kCT) void topk_chunked_kernel(Params p) {
   auto chunk_count = [&](int nv) { return chunks_of(p, nv); };
   Cursor cu;
   Item it;
-  // Phase 1a: histograms of this workgroup's chunks of several-chunk rows (the chunk items
+  // Phase 1: histograms of this workgroup's chunks of several-chunk rows (the chunk items
   // come first in the list, so the numbering of chunk items alone finds them).
   for (uint32_t m = 0;; ++m) {
     if (!locate(p, cu, sh, (uint32_t)min<uint64_t>(position(m), 0xFFFFFFFFu), it, chunk_count)) break;
@@ -961,10 +964,21 @@ __global__ __launch_bounds__(kCT) void topk_chunked_kernel(Params p) {
     __syncthreads();
     if (tid == 0) atomicAdd(&p.counters[4 * (int64_t)it.r + kCntHist], 1u);
   }
-  // Phase 1b: whole rows, class by class (their list positions follow the chunk items);
-  // trivial rows.
   // The item totals, after the chunks are counted (before any wait on other workgroups).
   const ItemTotals tot = item_totals(p, sh, cu);
+  // Phase 2: split this workgroup's chunks of several-chunk rows. Each chunk is loaded
+  // again (mostly from cache) before the wait for its row's histogram, so the load and
+  // the wait overlap.
+  rewind(p, cu);
+  for (uint32_t m = 0;; ++m) {
+    const uint64_t j = position(m);
+    if (j >= tot.chunks || !locate(p, cu, sh, (uint32_t)j, it, chunk_count)) break;
+    float v[kChunkPer];
+    fetch_chunk(p, it, v);
+    split_chunk(p, sh, it, v);
+  }
+  // Phase 3: whole rows, class by class (their list positions follow the chunk items);
+  // trivial rows.
   {
     const uint32_t nwhole = tot.whole[0] + tot.whole[1] + tot.whole[2] + tot.whole[3];
     Cursor cw;
@@ -1000,17 +1014,6 @@ __global__ __launch_bounds__(kCT) void topk_chunked_kernel(Params p) {
   for (int r = blockIdx.x; r < p.rows; r += gridDim.x) {
     const int nv = visible(p, r);
     if (nv <= p.k) select_trivial_row<kCT>(p, r, nv);
-  }
-  // Phase 2: split this workgroup's chunks of several-chunk rows. Each chunk is loaded
-  // again (mostly from cache) before the wait for its row's histogram, so the load and
-  // the wait overlap.
-  rewind(p, cu);
-  for (uint32_t m = 0;; ++m) {
-    const uint64_t j = position(m);
-    if (j >= tot.chunks || !locate(p, cu, sh, (uint32_t)j, it, chunk_count)) break;
-    float v[kChunkPer];
-    fetch_chunk(p, it, v);
-    split_chunk(p, sh, it, v);
   }
 }
 
