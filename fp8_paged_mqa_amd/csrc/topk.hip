@@ -639,13 +639,24 @@ __device__ __forceinline__ int whole_class(const Params& p, int nv) {
 
 // Walks the chunk items of a call in increasing order, rows kCT at a time: thread t holds
 // row base + t, its visible count, its chunk count and the exclusive prefix of the counts
-// in the block.
+// in the block. With every row in one block (rows <= kCT) the visible counts, once read,
+// are kept (held): later passes and other numberings reuse them instead of reading
+// context_lens again.
 struct Cursor {
   int base = -kCT;
   uint32_t first = 0, total = 0;  // items before the block, items in it
   uint32_t excl = 0, nch = 0;
   int nv = 0;
+  bool held = false;  // nv is row threadIdx.x's visible count (all rows in one block)
 };
+
+// A cursor at the start of another numbering, keeping the visible counts `from` holds.
+__device__ __forceinline__ Cursor restart(const Cursor& from) {
+  Cursor c;
+  c.nv = from.nv;
+  c.held = from.held;
+  return c;
+}
 
 struct Item {
   int r, c, nv, nch;
@@ -673,7 +684,8 @@ __device__ bool locate(const Params& p, Cursor& cu, Core<kCT>& sh, uint32_t item
     cu.base += kCT;
     if (cu.base >= p.rows) return false;
     const int row = cu.base + (int)threadIdx.x;
-    cu.nv = row < p.rows ? visible(p, row) : 0;
+    if (!cu.held) cu.nv = row < p.rows ? visible(p, row) : 0;  // uniform
+    cu.held = p.rows <= kCT;
     cu.nch = count(cu.nv);
     cu.excl = block_exclusive_scan<kCT>(cu.nch, sh, kRedLoc, cu.total);
     __syncthreads();  // every thread has read the scan scratch
@@ -891,7 +903,7 @@ __device__ ItemTotals item_totals(const Params& p, Core<kCT>& sh, const Cursor& 
   constexpr int W = kCT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const bool cached = p.rows <= kCT && cu.base == 0;  // uniform
+  const bool cached = cu.held;  // uniform
   ItemTotals t = {0u, {0u, 0u, 0u, 0u}};
   for (int base = 0; base < p.rows; base += kCT) {
     const int row = base + (int)threadIdx.x;
@@ -1004,7 +1016,7 @@ __global__ __launch_bounds__(kCT) void topk_chunked_kernel(Params p) {
         }
       }
       if (cls != cls_at) {  // a new numbering: start over
-        cw = Cursor();
+        cw = restart(cu);
         cls_at = cls;
       }
       if (!locate(p, cw, sh, w, it, [&](int nv) { return whole_class(p, nv) == cls ? 1u : 0u; })) break;
