@@ -109,6 +109,16 @@ def test_other_head_counts(heads, next_n):
     _parity(case, what=f"H={heads} N={next_n}")
 
 
+@pytest.mark.parametrize("heads,next_n", [(16, 2), (16, 3), (16, 4), (48, 2), (32, 3)])
+def test_half_stage_instances(heads, next_n):
+    """Every half-stage kernel (one wave holds all decode rows of a request, pages under 64
+    tokens) in a call too large for the small-call form: 40 requests."""
+    ctx = [1, 70, 2049, 300, 4100, 64, 65, 2048, 4095, 1000] * 4
+    case = wl.make_case(batch=len(ctx), next_n=next_n, heads=heads, ctx=ctx, max_model_len=4200,
+                        seed=3100 + heads + next_n)
+    _parity(case, what=f"half-stage H={heads} N={next_n}")
+
+
 @pytest.mark.parametrize("batch,max_ctx", [(64, 400), (65, 400), (300, 400), (5500, 40), (8192, 24)])
 def test_request_counts(batch, max_ctx):
     """Up to 64 requests each wave scans the context lengths itself (one per lane); above,
