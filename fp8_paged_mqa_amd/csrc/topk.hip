@@ -33,7 +33,8 @@
 //
 // Modes (nv is known only on the device):
 //   max_model_len <= 8192: one launch, workgroup r (1024 threads) selects row r whole, or
-//     writes it directly when nv <= k. No workspace.
+//     writes it directly when nv <= k, or drops the row's smallest element when nv = k + 1.
+//     No workspace.
 //   8192 < max_model_len <= 32768: one launch, workgroup r selects row r whole with 32
 //     values per thread. No workspace.
 //   max_model_len > 32768: one launch of the chunked kernel (one workgroup per CU). Rows
@@ -66,6 +67,7 @@ constexpr int kCoarseBins = 64;                   // chunked rows: top 6 key bit
 constexpr int kRowCap = 8192;                     // LDS candidates of a whole-row select (64 KB)
 constexpr int kChunkCap = kRowCap;                // LDS (and workspace) candidates of a chunked row
 constexpr int kRankMax = 256;                     // candidate lists up to this size are ranked
+constexpr int kMaxK = 2048;                       // largest k the library accepts
 
 struct Params {
   const float* logits;
@@ -534,13 +536,74 @@ __device__ void select_row(const Params& p, int r, int nv, Full<T, CAP>& sh) {
   }
 }
 
+// Rows with nv = k + 1 (the reproducer's shape: ctx = 2049 with k = 2048): every visible
+// position but the one with the smallest order key e is selected. One block minimum of e
+// (a butterfly over each wave, one barrier) finds it, and the other positions are written
+// in position order, position t to slot t or t - 1: no histogram, threshold or ranking.
+// Used by the short-row kernel (max_model_len <= 8192: decode bs=1 at ctx 2049 goes
+// 5.05 -> 4.1 us); the wide and chunked kernels keep their code as it is, which the extra
+// branch made slower (their register budgets are tighter).
+template <int T, int CAP>
+__device__ void drop_min_row(const Params& p, int r, int nv, Full<T, CAP>& sh) {
+  constexpr int W = T / 64;
+  constexpr int PER = 4;
+  static_assert(PER * T > kMaxK, "a row of k + 1 elements fits PER values per thread");
+  const float* row = p.logits + (int64_t)r * p.L;
+  int32_t* out = p.idx + (int64_t)r * p.k;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = (int)threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, nv * 4, 0x00020000);
+  const uint32_t last = (uint32_t)(nv - 1) * 4u;
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t off = min((uint32_t)tid * 4u + (uint32_t)(i * T * 4), last);
+    v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+  }
+  uint64_t mn = ~0ull;  // larger than every composed key
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int t = i * T + tid;
+    const uint64_t e = compose(order_key(v[i]), t);
+    mn = (t < nv && e < mn) ? e : mn;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)mn, o);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(mn >> 32), o);
+    const uint64_t x = ((uint64_t)hi << 32) | lo;
+    mn = x < mn ? x : mn;
+  }
+  if (lane == 0) {
+    sh.red[kRedLo * W + wave] = (uint32_t)(mn >> 32);
+    sh.red[kRedHi * W + wave] = (uint32_t)mn;
+  }
+  __syncthreads();
+  uint64_t bm = ~0ull;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const uint64_t x = ((uint64_t)sh.red[kRedLo * W + w] << 32) | sh.red[kRedHi * W + w];
+    bm = x < bm ? x : bm;
+  }
+  const int px = position(bm);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int t = i * T + tid;
+    if (t < nv && t != px) out[t - (t > px ? 1 : 0)] = t;
+  }
+}
+
 // Whole-row select with the fewest values per thread that hold the row: a phase costs
 // about one instruction per value a thread holds, and rows shorter than the kernel's
 // longest (clamped loads past nv only repeat the last value) need not pay for it. MAXPER is
 // the longest form a kernel needs.
-template <int T, int CAP, int MAXPER>
+template <int T, int CAP, int MAXPER, bool DROP_MIN = false>
 __device__ void select_row_fit(const Params& p, int r, int nv, Full<T, CAP>& sh) {
-  if (nv <= 4 * T) {  // uniform, like every branch here
+  if (DROP_MIN && nv == p.k + 1) {  // uniform, like every branch here
+    drop_min_row<T, CAP>(p, r, nv, sh);
+  } else if (nv <= 4 * T) {
     select_row<T, CAP, 4>(p, r, nv, sh);
   } else if (MAXPER <= 8 || nv <= 8 * T) {
     select_row<T, CAP, 8>(p, r, nv, sh);
@@ -558,7 +621,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(Params p) {
   const int r = blockIdx.x;
   const int nv = visible(p, r);
   if (nv <= p.k) select_trivial_row<kRowThreads>(p, r, nv);
-  else select_row_fit<kRowThreads, kRowCap, kPer>(p, r, nv, sh);
+  else select_row_fit<kRowThreads, kRowCap, kPer, true>(p, r, nv, sh);
 }
 
 // kRowLen < max_model_len <= kWideLen: one launch, workgroup r selects row r with 32
