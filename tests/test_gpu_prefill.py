@@ -75,3 +75,38 @@ def test_prefill_large_sampled():
     rows = np.unique(np.r_[0, 1, 15, 16, 17, 255, 1000, 2047, 2048, 4095, np.random.default_rng(93).integers(0, M, 14)])
     o = oracle.mqa_logits(q[rows], k, sc, w[rows], ks[rows], ke[rows])
     check_logits(g[rows], o, "prefill large (sampled rows)")
+
+
+def _draw_prefill_shapes(n=12):
+    """Seeded random prefill calls: M and N off every tile multiple, every supported head
+    count, windows mixing causal, arbitrary (empty, reversed, clipped) and full ones, and
+    an output row stride at or past N."""
+    rng = np.random.default_rng(20261203)
+    shapes = []
+    for _ in range(n):
+        M = int(rng.integers(1, 400))
+        N = int(rng.integers(1, 3000))
+        H = int(rng.choice([16, 32, 48, 64]))
+        kind = rng.choice(["causal", "random", "mixed"])
+        if kind == "causal":
+            ks = np.zeros(M, np.int64)
+            ke = np.arange(M) + (N - M) + 1
+        else:
+            ks = rng.integers(-40, N + 40, size=M)
+            ke = rng.integers(-40, N + 40, size=M)
+            if kind == "mixed":
+                full = rng.random(M) < 0.5
+                ks[full], ke[full] = 0, N
+        stride = N + int(rng.choice([0, 0, 1, 3, 37]))
+        shapes.append((M, N, H, ks, ke, stride, bool(rng.random() < 0.5), int(rng.integers(1 << 30))))
+    return shapes
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_prefill_random_shapes(i):
+    M, N, H, ks, ke, stride, neg, seed = _draw_prefill_shapes()[i]
+    q, k, sc, w = _inputs(M, N, H, seed=seed, neg_scales=neg)
+    say(f"[gpu] prefill random shape {i}: M={M} N={N} H={H} stride={stride}")
+    g = _run(q, k, sc, w, ks, ke, stride=stride)
+    check_logits(g[:, :N], oracle.mqa_logits(q, k, sc, w, ks, ke), f"prefill random shape {i}")
+    assert np.all(np.isnan(g[:, N:])), "columns past N must stay untouched"
