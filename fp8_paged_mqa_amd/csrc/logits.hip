@@ -50,12 +50,11 @@
 //     unconditionally (a dead stage or a table entry outside the cache reads row 0
 //     instead), and the prologue issues in the loop's order, so the loop is
 //     straight-line code and each compute waits only for its own stage's loads.
-//   * Half-stage form (pages under 64 tokens, one row group, up to 64 heads, a wave
-//     holding several decode rows): the two 32-token halves of the next stage are in
-//     flight (~8.4 KB) while a stage is computed, the weights sit in LDS, and one tile's
-//     operands and accumulators are live at a time, so even 8 row tiles fit 256 VGPRs
-//     and two workgroups share a CU: the same bytes in flight per CU, spread over twice
-//     the waves.
+//   * Half-stage form (pages under 64 tokens, up to 64 heads, a wave holding several
+//     decode rows): the two 32-token halves of the next stage are in flight (~8.4 KB)
+//     while a stage is computed, the weights sit in LDS, and one tile's operands and
+//     accumulators are live at a time, so even 8 row tiles fit 256 VGPRs and two
+//     workgroups share a CU: the same bytes in flight per CU, spread over twice the waves.
 //   * Epilogue in registers: the dequant scale's sign is folded into the fp8 key (flip
 //     the sign bit of every byte, exact; skipped when no scale of the tile is negative),
 //     so relu(scale*s) = |scale| * relu(sign*s) and |scale| multiplies once per token
@@ -764,10 +763,11 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
     // become one.
     fn = kTableSmall[tpj - 1][jpg - 1];
     per_cu = 2;
-  } else if (a.block_shift < 6 && p.groups == 1 && jpg > 1) {
-    // A wave holding several decode rows (pages under 64 tokens, up to 64 heads): the
-    // half-stage form, whose registers fit two workgroups per CU; with whole stages its
-    // query and key registers take the whole register file, one wave per SIMD.
+  } else if (a.block_shift < 6 && jpg > 1) {
+    // A wave holding several decode rows (pages under 64 tokens, up to 64 heads, one or
+    // more row groups): the half-stage form, whose registers fit two workgroups per CU;
+    // with whole stages its query and key registers take the whole register file, one
+    // wave per SIMD.
     fn = kTableHalf[tpj - 1][jpg - 1];
     per_cu = 2;
   } else if (a.block_shift >= 6 && p.groups > 1 && tpj * jpg <= 4) {

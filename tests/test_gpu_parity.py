@@ -109,10 +109,11 @@ def test_other_head_counts(heads, next_n):
     _parity(case, what=f"H={heads} N={next_n}")
 
 
-@pytest.mark.parametrize("heads,next_n", [(16, 2), (16, 3), (16, 4), (48, 2), (32, 3)])
+@pytest.mark.parametrize("heads,next_n", [(16, 2), (16, 3), (16, 4), (48, 2), (32, 3), (64, 4), (48, 3)])
 def test_half_stage_instances(heads, next_n):
-    """Every half-stage kernel (one wave holds all decode rows of a request, pages under 64
-    tokens) in a call too large for the small-call form: 40 requests."""
+    """Every half-stage kernel (a wave holds several decode rows of a request, pages under
+    64 tokens) in a call too large for the small-call form: 40 requests; the last two shapes
+    split each request's rows over two row groups."""
     ctx = [1, 70, 2049, 300, 4100, 64, 65, 2048, 4095, 1000] * 4
     case = wl.make_case(batch=len(ctx), next_n=next_n, heads=heads, ctx=ctx, max_model_len=4200,
                         seed=3100 + heads + next_n)
