@@ -50,8 +50,8 @@
 //     unconditionally (a dead stage or a table entry outside the cache reads row 0
 //     instead), and the prologue issues in the loop's order, so the loop is
 //     straight-line code and each compute waits only for its own stage's loads.
-//   * Half-stage form (pages under 64 tokens, up to 64 heads, a wave holding several
-//     decode rows): the two 32-token halves of the next stage are in flight (~8.4 KB)
+//   * Half-stage form (pages under 64 tokens, a wave holding several decode rows or more
+//     than 64 heads): the two 32-token halves of the next stage are in flight (~8.4 KB)
 //     while a stage is computed, the weights sit in LDS, and one tile's operands and
 //     accumulators are live at a time, so even 8 row tiles fit 256 VGPRs and two
 //     workgroups share a CU: the same bytes in flight per CU, spread over twice the waves.
@@ -207,8 +207,8 @@ __device__ __forceinline__ int locate(const int* a, int n, int x) {
 }
 
 // Up to 4 row tiles fit two waves per SIMD (<= 256 VGPRs); so do up to 8 in the half-stage
-// form (HALF: half a stage of keys per pipeline slot, weights in LDS). The other 5..8-tile
-// variants (H > 64, or several decode rows per wave) take the whole register file.
+// form (HALF: half a stage of keys per pipeline slot, weights in LDS). The whole-stage
+// 5..8-tile variants (64-token pages with H > 64) take the whole register file.
 template <int TPJ, int JPG, bool SMALL, bool HALF>
 __global__ __launch_bounds__(kThreads, (TPJ * JPG <= 4 || HALF) ? 2 : 1) void paged_logits_kernel(Params p) {
   constexpr int TILES = TPJ * JPG;  // MFMA row tiles (16 heads each) held by one wave
@@ -689,12 +689,16 @@ constexpr KernelFn kTableSmall[4][4] = {
     {kfs<4, 1>(), nullptr, nullptr, nullptr},
 };
 
-// Half-stage forms, [TPJ-1][JPG-1] for up to 64 heads and several decode rows per wave.
-constexpr KernelFn kTableHalf[4][4] = {
+// Half-stage forms, [TPJ-1][JPG-1]: several decode rows per wave, or more than 64 heads.
+constexpr KernelFn kTableHalf[8][4] = {
     {nullptr, kfh<1, 2>(), kfh<1, 3>(), kfh<1, 4>()},
     {nullptr, kfh<2, 2>(), kfh<2, 3>(), kfh<2, 4>()},
     {nullptr, kfh<3, 2>(), nullptr, nullptr},
     {nullptr, kfh<4, 2>(), nullptr, nullptr},
+    {kfh<5, 1>(), nullptr, nullptr, nullptr},
+    {kfh<6, 1>(), nullptr, nullptr, nullptr},
+    {kfh<7, 1>(), nullptr, nullptr, nullptr},
+    {kfh<8, 1>(), nullptr, nullptr, nullptr},
 };
 
 // Compute units of the current device, read once per device.
@@ -763,11 +767,11 @@ hipError_t launch_logits(const LogitsLaunch& a, hipStream_t stream) {
     // become one.
     fn = kTableSmall[tpj - 1][jpg - 1];
     per_cu = 2;
-  } else if (a.block_shift < 6 && jpg > 1) {
-    // A wave holding several decode rows (pages under 64 tokens, up to 64 heads, one or
-    // more row groups): the half-stage form, whose registers fit two workgroups per CU;
-    // with whole stages its query and key registers take the whole register file, one
-    // wave per SIMD.
+  } else if (a.block_shift < 6 && (jpg > 1 || tpj > 4)) {
+    // A wave holding several decode rows, or more than 64 heads (pages under 64 tokens):
+    // the half-stage form, whose registers fit two workgroups per CU (with whole stages
+    // the 5..8-tile waves take the whole register file, one wave per SIMD). Measured
+    // faster or equal on every shape tried: N = 2..4 at H = 32..80, H = 96 and 128 at N = 1.
     fn = kTableHalf[tpj - 1][jpg - 1];
     per_cu = 2;
   } else if (a.block_shift >= 6 && p.groups > 1 && tpj * jpg <= 4) {
