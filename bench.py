@@ -125,8 +125,13 @@ def bench_prefill(args):
     ke = (np.arange(M) + (N - M) + 1).astype(np.int32)
     copies = []
     for _ in range(C):
-        q = torch.from_numpy(workloads.to_e4m3fn_bytes(rng.standard_normal((M, H, 128), dtype=np.float32))).cuda()
-        k = torch.from_numpy(workloads.to_e4m3fn_bytes(rng.standard_normal((N, 128), dtype=np.float32))).cuda()
+        qf = rng.standard_normal((M, H, 128), dtype=np.float32)
+        kf = rng.standard_normal((N, 128), dtype=np.float32)
+        if args.prefill_data == "zero":  # same work on operands that do not switch
+            qf[:] = 0.0
+            kf[:] = 0.0
+        q = torch.from_numpy(workloads.to_e4m3fn_bytes(qf)).cuda()
+        k = torch.from_numpy(workloads.to_e4m3fn_bytes(kf)).cuda()
         sc = torch.from_numpy(rng.lognormal(0, 0.5, size=N).astype(np.float32)).cuda()
         w = torch.from_numpy(rng.standard_normal((M, H), dtype=np.float32)).cuda()
         out = torch.empty((M, N), dtype=torch.float32, device="cuda")
@@ -158,7 +163,8 @@ def bench_prefill(args):
         "metric": "non-paged (prefill) indexer logits, TFLOP/s of the contraction",
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": reps * C, "us_per_call": us,
         "higher_is_better": True, "dtype": "fp8e4m3fn->f16 mfma, f32 accumulate", "data": "synthetic",
-        "config": {"workload": f"M={M} query rows, N={N} keys, H={H}, causal windows", "m": M, "n": N, "heads": H},
+        "config": {"workload": f"M={M} query rows, N={N} keys, H={H}, causal windows", "m": M, "n": N, "heads": H,
+                   "operands": args.prefill_data},
         "hbm_gbps_algorithmic": nbytes / (us * 1e-6) / 1e9,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_F16_PEAK_TFLOPS, "kernel": "prefill_logits_kernel",
@@ -444,6 +450,9 @@ def main():
     ap.add_argument("--m", type=int, default=4096, help="query rows for --op prefill")
     ap.add_argument("--n", type=int, default=8192, help="keys for --op prefill")
     ap.add_argument("--heads", type=int, default=32, help="heads for --op prefill")
+    ap.add_argument("--prefill-data", default="random", choices=["random", "zero"],
+                    help="operand codes for --op prefill: random (the benchmark) or all zero (the clock the "
+                         "chip holds when the operands do not switch; same instructions and cycles)")
     ap.add_argument("--tokens", type=int, default=65536, help="tokens per call for --op kwrite")
     ap.add_argument("--calibrate-copy-mib", type=int, default=256,
                     help="size of the plain device copy run once for counter calibration (0: skip)")
