@@ -396,30 +396,53 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(Params p) {
 // thread) in one pass with a running maximum: per split, M' = max(M, m_s),
 // acc = acc * 2^(M - M') + 2^(m_s - M') * l_s * (O_s / l_s), L = L * 2^(M - M') + 2^(m_s - M') * l_s;
 // out = kv_scale * acc / L.
-// The loads of consecutive splits do not depend on each other, so they are in flight
-// together.
+// Splits are taken eight at a time: the eight states' loads are issued together (split
+// indices past the last repeat it and merge with weight 0), then merged in split order, so
+// a row of up to eight splits costs one memory round trip.
 __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(Params p) {
+  constexpr int kBatch = 8;
   const int h = blockIdx.x;
   const int r = blockIdx.y;
   const uint8_t* base = p.ws + (int64_t)r * p.splits * kPartialBytes;
   float M = -__builtin_inff();
   float L = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-  for (int s = 0; s < p.splits; ++s) {
-    const uint8_t* part = base + s * kPartialBytes;
-    const float* ml = reinterpret_cast<const float*>(part + kH * kDV * 2);
-    const float ms = ml[h];
-    const float ls = ml[kH + h];
-    const f16x4 oh = *reinterpret_cast<const f16x4*>(part + (h * kDV + 4 * threadIdx.x) * 2);
-    const f32x4 os = {(float)oh[0], (float)oh[1], (float)oh[2], (float)oh[3]};  // O_s / l_s
-    const float mn = __builtin_fmaxf(M, ms);
-    const float mu = mn == -__builtin_inff() ? 0.0f : mn;
-    const float a = __builtin_amdgcn_exp2f(M - mu);   // 0 while nothing has been seen
-    const float w = __builtin_amdgcn_exp2f(ms - mu) * ls;  // 0 for a split that saw nothing
-    acc = acc * a + os * w;
-    L = L * a + w;
-    M = mn;
+  for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
+    // Lane t of each wave loads split s0 + t's maximum and sum (vector loads, issued with
+    // the outputs' loads rather than as scalar loads the compiler would space out), then
+    // every lane reads them from lanes 0..7.
+    const float* mine = reinterpret_cast<const float*>(
+        base + (int64_t)min(s0 + (int)(threadIdx.x & (kBatch - 1)), p.splits - 1) * kPartialBytes + kH * kDV * 2);
+    const float m_t = mine[h];
+    const float l_t = mine[kH + h];
+    f16x4 oh[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const uint8_t* part = base + (int64_t)min(s0 + i, p.splits - 1) * kPartialBytes;
+      oh[i] = *reinterpret_cast<const f16x4*>(part + (h * kDV + 4 * threadIdx.x) * 2);
+    }
+    float ms[kBatch], ls[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      ms[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_t), i));
+      ls[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_t), i));
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      // A repeated index merges as a split that saw nothing (factor 1, weight 0). Branch-free,
+      // so that the compiler does not move the loads into the branches one by one.
+      const bool ok = s0 + i < p.splits;
+      const float msi = ok ? ms[i] : -__builtin_inff();
+      const float lsi = ok ? ls[i] : 0.0f;
+      const f32x4 os = {(float)oh[i][0], (float)oh[i][1], (float)oh[i][2], (float)oh[i][3]};  // O_s / l_s
+      const float mn = __builtin_fmaxf(M, msi);
+      const float mu = mn == -__builtin_inff() ? 0.0f : mn;
+      const float a = __builtin_amdgcn_exp2f(M - mu);  // 0 while nothing has been seen
+      const float w = __builtin_amdgcn_exp2f(msi - mu) * lsi;  // 0 for a split that saw nothing
+      acc = acc * a + os * w;
+      L = L * a + w;
+      M = mn;
+    }
   }
   const float f = L == 0.0f ? 0.0f : p.vscale / L;
   *reinterpret_cast<f32x4*>(p.out + ((int64_t)r * kH + h) * kDV + 4 * threadIdx.x) = acc * f;
