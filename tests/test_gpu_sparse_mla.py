@@ -88,6 +88,34 @@ def test_sparse_mla_random(B, N, ctx, topk, S):
     check(case, g, gl, *oracle_of(case), f"mla B={B} N={N} topk={topk} S={S}")
 
 
+def _draw_mla_shapes(n=16):
+    """Seeded random calls: batch, next_n 1..4, block sizes 1/16/64, topk from 1 to 2048
+    (so from one split per row to more than eight), contexts mixing uniform draws with
+    topk, topk + 1 and tile boundaries."""
+    rng = np.random.default_rng(20261205)
+    shapes = []
+    for _ in range(n):
+        N = int(rng.integers(1, 5))
+        S = int(rng.choice([1, 1, 16, 64]))
+        topk = int(rng.choice([1, 64, 100, 333, 512, 2048]))
+        B = max(1, min(int(rng.choice([1, 2, 3, 7, 16, 64])), 131072 // (N * topk)))
+        ctx = rng.integers(0, 6000, B)
+        pick = rng.random(B) < 0.3
+        ctx[pick] = rng.choice([0, 1, topk, topk + 1, 64, 65, 2048], int(pick.sum()))
+        shapes.append((B, N, np.maximum(ctx, N).tolist(), topk, S, int(rng.integers(1 << 30))))
+    return shapes
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_sparse_mla_random_drawn(i):
+    B, N, ctx, topk, S, seed = _draw_mla_shapes()[i]
+    case = wl.make_mla_case(batch=B, next_n=N, ctx=ctx, topk=topk, block_size=S, seed=seed)
+    what = f"mla drawn {i}: B={B} N={N} topk={topk} S={S}"
+    say(f"[gpu] {what}")
+    g, gl = run_gpu(case)
+    check(case, g, gl, *oracle_of(case), what)
+
+
 def test_sparse_mla_list_forms():
     """Empty rows, one position, duplicates, padding in the middle, a zero query."""
     case = wl.make_mla_case(batch=6, next_n=1, ctx=[300, 300, 300, 300, 300, 10], topk=130, seed=510)
